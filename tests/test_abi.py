@@ -1,0 +1,94 @@
+"""The C-ABI library loads and exports every entry point include/wq.h declares;
+invalid arguments are rejected on the host before any launch (CPU only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wq.h")
+LIB = os.path.join(ROOT, "weight_only_quantized_quant_amd", "libwq.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libwq.so is not built (run __graft_entry__.build())")
+    return ctypes.CDLL(LIB)
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("quantize_e4m3", "quantize_mxfp4", "quantize_int4", "wq_dequant", "wq_gemm",
+              "wq_gemm_workspace_size", "wq_status_string"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    lib.wq_status_string.restype = ctypes.c_char_p
+    for code in range(5):
+        assert lib.wq_status_string(code).startswith(b"WQ_")
+    assert b"unknown" in lib.wq_status_string(99)
+
+
+def test_binding_exposes_the_same_names():
+    import weight_only_quantized_quant_amd as W
+    for name in declared_functions():
+        assert callable(getattr(W, name)), name
+
+
+def _i64(v):
+    return ctypes.c_int64(v)
+
+
+def test_invalid_arguments_rejected_before_launch(lib):
+    f = lib.quantize_e4m3
+    f.restype = ctypes.c_int
+    p = ctypes.c_void_p(0x1000)          # never dereferenced: validation fails first
+    q = ctypes.c_void_p(0x1008)          # misaligned
+    # NULL input, bad shapes, odd columns
+    assert f(None, 1, _i64(4), _i64(64), 0, p, None, None) == 1
+    assert f(p, 1, _i64(0), _i64(64), 0, p, None, None) == 1
+    assert f(p, 1, _i64(4), _i64(12), 0, p, None, None) == 1
+    assert f(p, 7, _i64(4), _i64(64), 0, p, None, None) == 3          # unsupported dtype
+    assert f(q, 1, _i64(4), _i64(64), 0, p, None, None) == 2          # misaligned
+    assert f(p, 1, _i64(4), _i64(64), 48, p, p, None) == 3            # unsupported block
+    assert f(p, 1, _i64(4), _i64(64), 128, p, p, None) == 1           # cols % block
+    assert f(p, 1, _i64(4), _i64(64), 32, p, None, None) == 1         # scales needed
+    g = lib.quantize_mxfp4
+    g.restype = ctypes.c_int
+    assert g(p, 0, _i64(4), _i64(64), 8, p, p, None) == 3
+    assert g(p, 0, _i64(4), _i64(48), 32, p, p, None) == 1
+    h = lib.quantize_int4
+    h.restype = ctypes.c_int
+    assert h(p, 0, _i64(4), _i64(128), 96, p, p, None) == 3
+    assert h(p, 0, _i64(4), _i64(96), 64, p, p, None) == 1
+    d = lib.wq_dequant
+    d.restype = ctypes.c_int
+    assert d(p, 5, p, 0, 128, _i64(4), _i64(128), p, None) == 3       # int4 needs bf16 scales
+    assert d(p, 9, p, 1, 128, _i64(4), _i64(128), p, None) == 3
+    assert d(p, 5, p, 1, 128, _i64(4), _i64(100), p, None) == 1
+    gm = lib.wq_gemm
+    gm.restype = ctypes.c_int
+    args = lambda M, N, K, wdt, sdt, grp, x=p: (x, _i64(M), _i64(N), _i64(K), p, wdt, p, sdt, grp, p, None,
+                                               ctypes.c_size_t(0), None)
+    assert gm(*args(1, 16, 100, 5, 1, 128)) == 1                        # K % 128
+    assert gm(*args(0, 16, 128, 5, 1, 128)) == 1
+    assert gm(*args(1, 16, 128, 5, 1, 96)) == 3                         # bad group
+    assert gm(*args(1, 16, 128, 3, 1, 32)) == 3                         # fp4 needs E8M0
+    assert gm(*args(1, 16, 256, 2, 0, 128)) == 3                        # e4m3 needs group == K
+    assert gm(*args(1, 16, 128, 5, 1, 128, x=q)) == 2
+    lib.wq_gemm_workspace_size.restype = ctypes.c_size_t
+    assert lib.wq_gemm_workspace_size(_i64(1), _i64(16), _i64(128), 5, 128) == 0

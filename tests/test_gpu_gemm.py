@@ -1,0 +1,137 @@
+"""GPU parity of wq_gemm (decode GEMV and prefill GEMM) against the oracle's
+fp64 reference, with the acceptance bound
+    |y - y_ref| <= 8e-3 |y_ref| + 1e-3 sum_k |x_k w_k|
+per element.  Weights are quantized by the oracle (inputs never come from the
+GPU path)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import dequant as OD
+from oracle import e4m3 as OE
+from oracle import gemm as OG
+from oracle import int4 as OI
+from oracle import mxfp4 as OM
+from oracle.formats import bf16_decode
+from synthetic import decode_inputs, mxfp4_gemv_inputs, prefill_inputs, to_bf16_bits
+from tests.gpu_helpers import banner, dev_bf16, dev_f32, dev_u8, dev_words, host_bits16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def W():
+    import weight_only_quantized_quant_amd as W
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return W
+
+
+def _prep(W, kind, Wf, group=128):
+    """Quantize fp32 weights with the oracle; return (device args, oracle bf16 operand, chan scale)."""
+    if kind == "int4":
+        packed, sb, _ = OI.quantize_int4(Wf, group)
+        args = (dev_words(packed), W.WQ_INT4X8, dev_bf16(sb), W.WQ_BF16, group)
+        return args, OD.dequant_int4(packed, sb, group), None
+    if kind == "mxfp4":
+        codes, sc = OM.quantize_mxfp4(Wf, 32)
+        args = (dev_u8(codes), W.WQ_E2M1X2, dev_u8(sc), W.WQ_E8M0, 32)
+        return args, OD.dequant_mxfp4(codes, sc, 32), None
+    codes, s = OE.quantize_e4m3(Wf, -1)
+    args = (dev_u8(codes), W.WQ_E4M3, dev_f32(s[:, 0]), W.WQ_F32, Wf.shape[1])
+    return args, OD.dequant_e4m3(codes), s[:, 0]
+
+
+def _check(y_dev, xbits, wdeq, chan, rows=None):
+    y = bf16_decode(host_bits16(y_dev))
+    xb = xbits if rows is None else xbits[rows]
+    if rows is not None:
+        y = y[rows]
+    ref, asum = OG.reference(xb, wdeq, chan)
+    ratio = OG.worst_ratio(y, ref, asum)
+    assert np.isfinite(y).all()
+    assert ratio <= 1.0, f"worst error / bound = {ratio:.3f}"
+    return ratio
+
+
+@pytest.mark.parametrize("kind", ["int4", "mxfp4", "e4m3"])
+@pytest.mark.parametrize("M,N,K", [(1, 1000, 384), (3, 520, 512), (16, 272, 1024), (5, 17, 128), (2, 4096, 2048)])
+def test_gemv_ragged(W, kind, M, N, K):
+    g = np.random.default_rng(M * 1000 + N + K)
+    Wf = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
+    Wf[:, g.choice(K, 3, replace=False)] *= 40
+    xbits = to_bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    args, wdeq, chan = _prep(W, kind, Wf)
+    banner("gemv", kind, M, N, K)
+    y = W.wq_gemm(dev_bf16(xbits), *args, N)
+    _check(y, xbits, wdeq, chan)
+
+
+@pytest.mark.parametrize("group", [32, 64])
+def test_gemv_int4_small_groups(W, group):
+    g = np.random.default_rng(group)
+    Wf = (g.standard_normal((300, 512)) * 0.02).astype(np.float32)
+    xbits = to_bf16_bits(g.standard_normal((4, 512)).astype(np.float32))
+    args, wdeq, chan = _prep(W, "int4", Wf, group)
+    banner("gemv int4 group", group)
+    _check(W.wq_gemm(dev_bf16(xbits), *args, 300), xbits, wdeq, chan)
+
+
+def test_gemv_mxfp4_small_config(W):
+    xbits, Wf = mxfp4_gemv_inputs(0)
+    args, wdeq, chan = _prep(W, "mxfp4", Wf)
+    banner("gemv mxfp4 1x512 . 1024x512")
+    _check(W.wq_gemm(dev_bf16(xbits), *args, 1024), xbits, wdeq, chan)
+
+
+@pytest.fixture(scope="module")
+def decode_weights(W):
+    _, Wf = decode_inputs(1, 0)
+    return {k: _prep(W, k, Wf) for k in ("int4", "e4m3")}
+
+
+@pytest.mark.parametrize("kind", ["int4", "e4m3"])
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_decode_full_size(W, decode_weights, kind, M):
+    xbits, _ = decode_inputs(M, seed=10 + M, with_weight=False)
+    args, wdeq, chan = decode_weights[kind]
+    banner("decode full size", kind, "M", M)
+    y = W.wq_gemm(dev_bf16(xbits), *args, 14336)
+    y2 = W.wq_gemm(dev_bf16(xbits), *args, 14336)
+    assert torch.equal(y, y2)                                       # fixed reduction order
+    _check(y, xbits, wdeq, chan)
+
+
+@pytest.mark.parametrize("kind", ["int4", "mxfp4", "e4m3"])
+@pytest.mark.parametrize("M,N,K", [(300, 520, 512), (17, 256, 256), (512, 512, 1024), (257, 33, 128)])
+def test_gemm_ragged(W, kind, M, N, K):
+    g = np.random.default_rng(M + N + K)
+    Wf = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
+    xbits = to_bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    args, wdeq, chan = _prep(W, kind, Wf)
+    banner("gemm", kind, M, N, K)
+    _check(W.wq_gemm(dev_bf16(xbits), *args, N), xbits, wdeq, chan)
+
+
+def test_prefill_full_size_sampled_rows(W):
+    xbits, Wf = prefill_inputs(0)
+    args, wdeq, chan = _prep(W, "mxfp4", Wf)
+    banner("prefill full size mxfp4 8192x4096 . 14336x4096")
+    y = W.wq_gemm(dev_bf16(xbits), *args, 14336)
+    rows = np.sort(np.random.default_rng(99).choice(8192, 192, replace=False))
+    rows = np.unique(np.concatenate([rows, [0, 255, 256, 8191]]))
+    _check(y, xbits, wdeq, chan, rows=rows)
+
+
+@pytest.mark.parametrize("M", [1, 64])
+def test_fp32_accumulation_all_ones(W, M):
+    # K = 4096 ones: an fp32 accumulator gives exactly 4096; bf16 would stall at 256
+    K, N = 4096, 64
+    xbits = to_bf16_bits(np.ones((M, K), np.float32))
+    codes = np.full((N, K), 0x38, np.uint8)                      # E4M3 1.0
+    banner("accumulation all ones", M)
+    y = W.wq_gemm(dev_bf16(xbits), dev_u8(codes), W.WQ_E4M3, dev_f32(np.ones(N, np.float32)), W.WQ_F32, K, N)
+    assert np.all(bf16_decode(host_bits16(y)) == 4096.0)
+    fp4 = np.full((N, K // 2), 0x22, np.uint8)                   # E2M1 1.0, 1.0
+    y = W.wq_gemm(dev_bf16(xbits), dev_u8(fp4), W.WQ_E2M1X2, dev_u8(np.full((N, K // 32), 127, np.uint8)),
+                  W.WQ_E8M0, 32, N)
+    assert np.all(bf16_decode(host_bits16(y)) == 4096.0)

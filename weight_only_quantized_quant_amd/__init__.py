@@ -1,0 +1,192 @@
+"""MI355X (gfx950) block-scaled quantizers and weight-only quantized matmul.
+
+Thin Python binding over the C ABI of ``libwq.so`` (declared in include/wq.h).
+The functions here carry the same names as the C entry points and only
+marshal arguments: they check devices, dtypes, shapes and contiguity of
+PyTorch tensors, allocate outputs with PyTorch when none are given, and pass
+raw device pointers plus the current HIP stream.  Every step of the
+computation runs in the HIP kernels; there is no other code path.  If the
+library has not been built the import fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwq.so")
+
+# dtype enum of the C ABI
+WQ_F32, WQ_BF16, WQ_E4M3, WQ_E2M1X2, WQ_E8M0, WQ_INT4X8 = range(6)
+WQ_OK, WQ_EINVAL, WQ_EALIGN, WQ_EUNSUPPORTED, WQ_EHIP = range(5)
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m weight_only_quantized_quant_amd.build` "
+        "(hipcc, gfx950). There is no fallback path.")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+_SIGS = {
+    "wq_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "quantize_e4m3": ([_vp, ctypes.c_int, _i64, _i64, _i32, _vp, _vp, _vp], ctypes.c_int),
+    "quantize_mxfp4": ([_vp, ctypes.c_int, _i64, _i64, _i32, _vp, _vp, _vp], ctypes.c_int),
+    "quantize_int4": ([_vp, ctypes.c_int, _i64, _i64, _i32, _vp, _vp, _vp], ctypes.c_int),
+    "wq_dequant": ([_vp, ctypes.c_int, _vp, ctypes.c_int, _i32, _i64, _i64, _vp, _vp], ctypes.c_int),
+    "wq_gemm": ([_vp, _i64, _i64, _i64, _vp, ctypes.c_int, _vp, ctypes.c_int, _i32, _vp, _vp, _sz, _vp],
+                ctypes.c_int),
+    "wq_gemm_workspace_size": ([_i64, _i64, _i64, ctypes.c_int, _i32], _sz),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _fn = getattr(lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+
+class WQError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {lib.wq_status_string(status).decode()}")
+
+
+def _check(status: int, where: str) -> None:
+    if status == WQ_OK:
+        return
+    if status in (WQ_EINVAL, WQ_EALIGN, WQ_EUNSUPPORTED):
+        err = WQError(status, where)
+        raise ValueError(str(err)) from err
+    raise WQError(status, where)
+
+
+def wq_status_string(status: int) -> str:
+    return lib.wq_status_string(status).decode()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str) -> None:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _x_dtype(x: torch.Tensor) -> int:
+    if x.dtype == torch.float32:
+        return WQ_F32
+    if x.dtype == torch.bfloat16:
+        return WQ_BF16
+    raise ValueError("input must be float32 or bfloat16")
+
+
+def _out(t, shape, dtype, device, name):
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _dev(t, name)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} of shape {tuple(shape)}")
+    return t
+
+
+def quantize_e4m3(x: torch.Tensor, block: int, codes=None, scales=None):
+    """x: 2-D fp32/bf16.  block 0 (plain cast), >0 (per 1 x block) or -1 (per row).
+    Returns (codes uint8 [rows, cols], scales fp32 [rows, groups] or None)."""
+    _dev(x, "x")
+    rows, cols = x.shape
+    codes = _out(codes, (rows, cols), torch.uint8, x.device, "codes")
+    if block == 0:
+        scales_ptr = None
+    else:
+        groups = 1 if block == -1 else (cols // block if block > 0 else 0)
+        scales = _out(scales, (rows, groups), torch.float32, x.device, "scales")
+        scales_ptr = scales.data_ptr()
+    _check(lib.quantize_e4m3(x.data_ptr(), _x_dtype(x), rows, cols, block, codes.data_ptr(), scales_ptr, _stream()),
+           "quantize_e4m3")
+    return codes, (scales if block != 0 else None)
+
+
+def quantize_mxfp4(x: torch.Tensor, block: int = 32, codes=None, scales=None):
+    """x: 2-D fp32/bf16 -> (codes uint8 [rows, cols/2], E8M0 scales uint8 [rows, cols/block])."""
+    _dev(x, "x")
+    rows, cols = x.shape
+    if block not in (16, 32) or cols % 32:
+        raise ValueError("block must be 16 or 32 and cols a multiple of 32")
+    codes = _out(codes, (rows, cols // 2), torch.uint8, x.device, "codes")
+    scales = _out(scales, (rows, cols // block), torch.uint8, x.device, "scales")
+    _check(lib.quantize_mxfp4(x.data_ptr(), _x_dtype(x), rows, cols, block, codes.data_ptr(), scales.data_ptr(),
+                              _stream()), "quantize_mxfp4")
+    return codes, scales
+
+
+def quantize_int4(w: torch.Tensor, group: int = 128, packed=None, scales=None):
+    """w: 2-D fp32/bf16 [N, K] -> (packed int32 [N, K/8] holding INT4X8 words,
+    bf16 scales [N, K/group])."""
+    _dev(w, "w")
+    rows, cols = w.shape
+    if group not in (32, 64, 128) or cols % group:
+        raise ValueError("group must be 32, 64 or 128 and divide cols")
+    packed = _out(packed, (rows, cols // 8), torch.int32, w.device, "packed")
+    scales = _out(scales, (rows, cols // group), torch.bfloat16, w.device, "scales")
+    _check(lib.quantize_int4(w.data_ptr(), _x_dtype(w), rows, cols, group, packed.data_ptr(), scales.data_ptr(),
+                             _stream()), "quantize_int4")
+    return packed, scales
+
+
+_W_ELEM_BYTES2 = {WQ_INT4X8: 1, WQ_E2M1X2: 1, WQ_E4M3: 2}   # bytes per 2 elements
+
+
+def _check_weight(wq, w_dtype, N, K):
+    _dev(wq, "wq")
+    if w_dtype not in _W_ELEM_BYTES2:
+        raise ValueError("unsupported weight dtype")
+    need = N * K * _W_ELEM_BYTES2[w_dtype] // 2
+    if wq.numel() * wq.element_size() != need:
+        raise ValueError(f"wq holds {wq.numel() * wq.element_size()} bytes, expected {need} for N={N}, K={K}")
+
+
+def _check_scales(sc, s_dtype, N, K, group):
+    if sc is None:
+        return None
+    _dev(sc, "w_scales")
+    per = {WQ_BF16: 2, WQ_E8M0: 1, WQ_F32: 4}[s_dtype]
+    count = N if s_dtype == WQ_F32 else N * (K // group)
+    if sc.numel() * sc.element_size() != count * per:
+        raise ValueError("w_scales has the wrong size")
+    return sc.data_ptr()
+
+
+def wq_dequant(wq: torch.Tensor, w_dtype: int, w_scales, s_dtype: int, group: int, N: int, K: int, out=None):
+    """Packed weights + scales -> bf16 [N, K] (the matmul's operand)."""
+    _check_weight(wq, w_dtype, N, K)
+    sp = _check_scales(w_scales, s_dtype, N, K, group) if w_scales is not None else None
+    out = _out(out, (N, K), torch.bfloat16, wq.device, "out")
+    _check(lib.wq_dequant(wq.data_ptr(), w_dtype, sp, s_dtype, group, N, K, out.data_ptr(), _stream()), "wq_dequant")
+    return out
+
+
+def wq_gemm_workspace_size(M: int, N: int, K: int, w_dtype: int, group: int) -> int:
+    return int(lib.wq_gemm_workspace_size(M, N, K, w_dtype, group))
+
+
+def wq_gemm(x: torch.Tensor, wq: torch.Tensor, w_dtype: int, w_scales: torch.Tensor, s_dtype: int, group: int,
+            N: int, y=None, workspace=None):
+    """y[M, N] = x[M, K] . dequant(wq)^T in bf16 with fp32 accumulation."""
+    _dev(x, "x")
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise ValueError("x must be a 2-D bfloat16 tensor")
+    M, K = x.shape
+    _check_weight(wq, w_dtype, N, K)
+    sp = _check_scales(w_scales, s_dtype, N, K, group)
+    y = _out(y, (M, N), torch.bfloat16, x.device, "y")
+    ws_ptr, ws_bytes = (None, 0)
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check(lib.wq_gemm(x.data_ptr(), M, N, K, wq.data_ptr(), w_dtype, sp, s_dtype, group, y.data_ptr(), ws_ptr,
+                       ws_bytes, _stream()), "wq_gemm")
+    return y

@@ -1,0 +1,190 @@
+// Device helpers for the gfx950 quantizer and matmul kernels.
+//
+// Hardware conversions used here (each checked bit-for-bit against the CPU
+// definitions of the formats by the test-suite):
+//   v_cvt_pk_bf16_f32            fp32 pair -> bf16 pair, round to nearest even
+//   v_cvt_pk_fp8_f32             fp32 pair -> OCP E4M3 pair, RNE; it does NOT
+//                                saturate (|x| > 464 gives NaN), so callers clamp
+//   v_cvt_scalef32_pk_fp4_f32    fp32 pair -> E2M1 pair of x / 2^(e-127), RNE,
+//                                saturating at 6; e = exponent field of `scale`
+//   v_cvt_scalef32_pk_bf16_fp4   E2M1 pair -> bf16 pair of v * 2^(e-127), exact
+//   v_cvt_scalef32_pk_bf16_fp8   E4M3 pair -> bf16 pair of v * 2^(e-127), exact
+// For the scaled forms only the exponent field e of the fp32 scale operand is
+// used, i.e. the scale acts as an E8M0 code (e = 0 means 2^-127).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short s16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+namespace wq {
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+
+// Two fp32 -> packed bf16 pair (a in the low half), RNE.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2_t v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float a) { return pack_bf16x2(a, a) & 0xFFFFu; }
+
+// E2M1 pair from byte `sel` of `w` -> bf16 pair scaled by 2^(code-127).
+template <int SEL>
+__device__ __forceinline__ uint32_t dq_fp4_pair(uint32_t w, float scale_as_e8m0) {
+  bf16x2_t v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale_as_e8m0, SEL);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// E4M3 pair from half `HI` of `w` -> exact bf16 pair.
+template <bool HI>
+__device__ __forceinline__ uint32_t dq_fp8_pair(uint32_t w) {
+  bf16x2_t v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// fp32 scale operand whose exponent field is the E8M0 code c (c = 0 -> 0.0f,
+// which the scaled conversions read as 2^-127).
+__device__ __forceinline__ float e8m0_as_scale(uint32_t c) { return __uint_as_float(c << 23); }
+
+// Exponent-first 0.75-threshold E8M0 rule on the fp32 pattern of max|x|.
+__device__ __forceinline__ uint32_t e8m0_code(float vmax) {
+  uint32_t bits = __float_as_uint(vmax) & 0x7FFFFFFFu;
+  uint32_t be = ((bits + (1u << 21)) & 0xFF800000u) >> 23;
+  return be > 2u ? be - 2u : 0u;
+}
+
+// INT4 dequantization of one packed word (8 two's-complement nibbles) with
+// bf16-valued group scale s: out[i] holds bf16(q_2i * s), bf16(q_2i+1 * s).
+//
+// Each nibble n is placed in the mantissa of a float with unit exponent,
+// f = 1 + u * 2^(p-23) with u = n ^ 8 = q + 8 the offset-binary nibble at bit
+// position p in {8, 12, 16}; then fma(f, s * 2^(23-p), -(2^(23-p) + 8) * s)
+// equals (u - 8) * s = q * s exactly (both constants are exact fp32 numbers
+// because s has 8 significant bits), and one RNE conversion makes bf16(q*s).
+struct Int4Consts {
+  float a8, b8, a12, b12, a16, b16;
+};
+__device__ __forceinline__ Int4Consts int4_consts(float s) {
+  Int4Consts c;
+  c.a8 = s * 32768.0f;  c.b8 = s * -32776.0f;
+  c.a12 = s * 2048.0f;  c.b12 = s * -2056.0f;
+  c.a16 = s * 128.0f;   c.b16 = s * -136.0f;
+  return c;
+}
+__device__ __forceinline__ float int4_elem(uint32_t src, uint32_t mask, float a, float b) {
+  return __builtin_fmaf(__uint_as_float((src & mask) | 0x3F800000u), a, b);
+}
+__device__ __forceinline__ void dq_int4_word(uint32_t w, const Int4Consts& c, uint32_t out[4]) {
+  const uint32_t u = w ^ 0x88888888u;
+  const uint32_t lo = u << 8;    // nibbles 0,1 -> bit positions 8,12
+  const uint32_t hi = u >> 12;   // nibbles 5,6,7 -> bit positions 8,12,16
+  const float e0 = int4_elem(lo, 0xF00u, c.a8, c.b8);
+  const float e1 = int4_elem(lo, 0xF000u, c.a12, c.b12);
+  const float e2 = int4_elem(u, 0xF00u, c.a8, c.b8);
+  const float e3 = int4_elem(u, 0xF000u, c.a12, c.b12);
+  const float e4 = int4_elem(u, 0xF0000u, c.a16, c.b16);
+  const float e5 = int4_elem(hi, 0xF00u, c.a8, c.b8);
+  const float e6 = int4_elem(hi, 0xF000u, c.a12, c.b12);
+  const float e7 = int4_elem(hi, 0xF0000u, c.a16, c.b16);
+  out[0] = pack_bf16x2(e0, e1);
+  out[1] = pack_bf16x2(e2, e3);
+  out[2] = pack_bf16x2(e4, e5);
+  out[3] = pack_bf16x2(e6, e7);
+}
+
+// Same result for any finite s: the magic-constant route above needs
+// s * 2^15 to stay finite, and for s <= 0 it would give +0 where q * s is -0,
+// so those scales take the direct route (sign-extend each nibble, exact fp32
+// product q * s, one RNE conversion).
+__device__ __forceinline__ void dq_int4_word_direct(uint32_t w, float s, uint32_t out[4]) {
+  float e[8];
+#pragma unroll
+  for (int j = 0; j < 8; j++) e[j] = (float)(((int32_t)(w << (28 - 4 * j))) >> 28) * s;
+#pragma unroll
+  for (int j = 0; j < 4; j++) out[j] = pack_bf16x2(e[2 * j], e[2 * j + 1]);
+}
+__device__ __forceinline__ bool int4_scale_fast(float s) { return s > 0.0f && s <= 0x1p100f; }
+
+// E2M1 word (8 codes) with E8M0 scale operand -> 4 bf16 pairs.
+__device__ __forceinline__ void dq_fp4_word(uint32_t w, float sc, uint32_t out[4]) {
+  out[0] = dq_fp4_pair<0>(w, sc);
+  out[1] = dq_fp4_pair<1>(w, sc);
+  out[2] = dq_fp4_pair<2>(w, sc);
+  out[3] = dq_fp4_pair<3>(w, sc);
+}
+
+// Correctly rounded fp32 quotient x / s given y = RN(1/s), for s in
+// [2^-90, 2^90] (Markstein's correction step: with y within half an ulp of 1/s
+// and q within one ulp of x/s, RN(q + (x - q s) y) = RN(x / s); the remainder is
+// exact through the fma).  Quotients whose magnitude is below 2^-11 may be off
+// by an ulp, which cannot change an E4M3 code (they all round to 0).  The
+// quotient takes the sign of x (s > 0): the correction step would otherwise
+// turn x = -0 into +0 (it adds +0 and -0).
+__device__ __forceinline__ float div_rn_markstein(float x, float s, float y) {
+  const float q = x * y;
+  const float r = __builtin_fmaf(-q, s, x);
+  return __builtin_copysignf(__builtin_fmaf(r, y, q), x);
+}
+
+__device__ __forceinline__ float clamp448(float v) { return __builtin_fminf(__builtin_fmaxf(v, -448.0f), 448.0f); }
+
+// Two fp32 -> E4M3 byte pair written into half HI of `old` (no saturation: the
+// inputs must already lie in [-464, 464]).
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3_pack2(float a, float b, uint32_t old) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
+}
+
+// Two fp32 -> E2M1 pair of v / 2^(c-127) into byte SEL of `old`.
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1_pack2(uint32_t old, float a, float b, float scale_as_e8m0) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, scale_as_e8m0, SEL);
+}
+
+// Loads of 8 consecutive input elements as fp32 (bf16 inputs widened exactly).
+__device__ __forceinline__ void load8_f32(const float* p, float v[8]) {
+  const u32x4_t a = *reinterpret_cast<const u32x4_t*>(p);
+  const u32x4_t b = *reinterpret_cast<const u32x4_t*>(p + 4);
+  v[0] = __uint_as_float(a[0]); v[1] = __uint_as_float(a[1]); v[2] = __uint_as_float(a[2]); v[3] = __uint_as_float(a[3]);
+  v[4] = __uint_as_float(b[0]); v[5] = __uint_as_float(b[1]); v[6] = __uint_as_float(b[2]); v[7] = __uint_as_float(b[3]);
+}
+__device__ __forceinline__ void load8_bf16(const uint16_t* p, float v[8]) {
+  const u32x4_t a = *reinterpret_cast<const u32x4_t*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    v[2 * i] = bf16_lo(a[i]);
+    v[2 * i + 1] = bf16_hi(a[i]);
+  }
+}
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* base, int64_t idx, float v[8]) {
+  if constexpr (BF16) load8_bf16(reinterpret_cast<const uint16_t*>(base) + idx, v);
+  else load8_f32(reinterpret_cast<const float*>(base) + idx, v);
+}
+
+__device__ __forceinline__ float absmax8(const float v[8]) {
+  float m = __builtin_fabsf(v[0]);
+#pragma unroll
+  for (int i = 1; i < 8; i++) m = __builtin_fmaxf(m, __builtin_fabsf(v[i]));
+  return m;
+}
+
+// Max over aligned groups of `width` consecutive lanes (width a power of two <= 64).
+__device__ __forceinline__ float group_max(float v, int width) {
+  for (int off = 1; off < width; off <<= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+}  // namespace wq
