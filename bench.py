@@ -1,0 +1,389 @@
+"""Benchmark of the weight-only quantized matmul and the block-scaled quantizers
+on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only CASE] [--no-cpu]
+
+One step is one decode GEMV y = x . dequant(Wq)^T at M = 1, K = 4096,
+N = 14336 with symmetric INT4 weights (bf16 scales per 128-element group),
+bf16 activations and output -- the decode W4A16 workload.  The weights are
+quantized on the GPU by quantize_int4 and replicated into 24 resident copies
+(727 MB) that the steps cycle through, so that the 256 MB Infinity Cache
+cannot serve them: every step streams its weights from HBM.  The K timed
+steps are launched as one HIP graph replay, bracketed by device
+synchronisation; `value` is algorithmic bytes / time.
+
+The same JSON line carries the roofline of that kernel (HIP events over the
+timed region on the launch stream), the oracle timed on the host (`cpu_baseline`)
+and `secondary` measurements: decode at M = 4 and 16, W8A16, prefill MXFP4 at
+M = 8192 (TFLOP/s), the activation quantizers at 4096 x 7168, the MXFP4 weight
+quantizer, a streaming copy and torch.matmul (hipBLASLt) at the prefill shape
+as secondary denominators.
+
+--only CASE runs a single case without the JSON summary (for rocprofv3):
+decode, decode_w8, prefill, quant_e4m3, quant_mxfp4, copy.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+ROTATE_BYTES = 700e6           # > 2.5x the 256 MB Infinity Cache
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--only", default=None)
+    p.add_argument("--reps", type=int, default=0, help="launches for --only (default per case)")
+    p.add_argument("--no-cpu", action="store_true")
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# helpers
+# ---------------------------------------------------------------------------
+
+def dev_bf16(torch, bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def graph_of(torch, fns):
+    """Capture the callables (each enqueues one launch) into one HIP graph."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fns[0]()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(torch, g, launches):
+    """HIP events on the current stream around one replay; ms per launch."""
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    g.replay()
+    b.record()
+    b.synchronize()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / launches
+
+
+def time_eager(torch, fn, reps, warm=2):
+    for _ in range(warm):
+        fn(0)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(reps):
+        fn(i)
+    b.record()
+    b.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("wq_gemm.hip", "wq_device.h", "wq_quant.hip"):
+        with open(os.path.join(ROOT, "weight_only_quantized_quant_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(case, bytes_per_launch):
+    """HBM traffic from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel sources; None otherwise."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(case)
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+
+class Decode:
+    """x[M, 4096] . dequant(W[14336, 4096])^T, INT4 g128 or E4M3 per-channel."""
+
+    def __init__(self, torch, W, M, kind="int4", K=4096, N=14336):
+        from synthetic import decode_inputs
+        self.torch, self.W, self.M, self.K, self.N, self.kind = torch, W, M, K, N, kind
+        xbits, Wf = decode_inputs(M, seed=0)
+        self.x = dev_bf16(torch, xbits)
+        wdev = torch.from_numpy(Wf).cuda()
+        if kind == "int4":
+            packed, sb = W.quantize_int4(wdev, 128)
+            self.wbytes = packed.numel() * 4 + sb.numel() * 2
+            base = (packed, sb)
+            self.meta = (W.WQ_INT4X8, W.WQ_BF16, 128)
+        else:
+            codes, sc = W.quantize_e4m3(wdev, -1)
+            sc = sc.reshape(-1).contiguous()
+            self.wbytes = codes.numel() + sc.numel() * 4
+            base = (codes, sc)
+            self.meta = (W.WQ_E4M3, W.WQ_F32, K)
+        del wdev
+        ncopy = max(1, int(ROTATE_BYTES // self.wbytes) + 1)
+        self.copies = [base] + [(base[0].clone(), base[1].clone()) for _ in range(ncopy - 1)]
+        self.y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        self.bytes = self.wbytes + M * K * 2 + M * N * 2
+        self.flops = 2.0 * M * N * K
+
+    def launch(self, i):
+        wq, sc = self.copies[i % len(self.copies)]
+        wdt, sdt, grp = self.meta
+        self.W.wq_gemm(self.x, wq, wdt, sc, sdt, grp, self.N, y=self.y)
+
+
+class Prefill:
+    """x[8192, 4096] . dequant(W_mxfp4[14336, 4096])^T."""
+
+    def __init__(self, torch, W, M=8192, K=4096, N=14336):
+        from synthetic import prefill_inputs
+        self.torch, self.W, self.M, self.K, self.N = torch, W, M, K, N
+        xbits, Wf = prefill_inputs(0, M=M, K=K, N=N)
+        self.x = dev_bf16(torch, xbits)
+        wdev = torch.from_numpy(Wf).cuda()
+        self.codes, self.sc = W.quantize_mxfp4(wdev, 32)
+        del wdev
+        self.y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        self.flops = 2.0 * M * N * K
+        self.bytes = self.codes.numel() + self.sc.numel() + M * K * 2 + M * N * 2
+
+    def launch(self, i):
+        self.W.wq_gemm(self.x, self.codes, self.W.WQ_E2M1X2, self.sc, self.W.WQ_E8M0, 32, self.N, y=self.y)
+
+
+class ActQuant:
+    """4096 x 7168 bf16 -> E4M3 per 1x128 (fp32 scales) or MXFP4 per 16 (E8M0)."""
+
+    def __init__(self, torch, W, kind):
+        from synthetic import act_quant_inputs
+        self.torch, self.W, self.kind = torch, W, kind
+        bits = act_quant_inputs(0)
+        x = dev_bf16(torch, bits)
+        rows, cols = bits.shape
+        inb = rows * cols * 2
+        if kind == "e4m3":
+            outb = rows * cols + rows * (cols // 128) * 4
+        else:
+            outb = rows * cols // 2 + rows * (cols // 16)
+        self.bytes = inb + outb
+        ncopy = max(1, int(ROTATE_BYTES // self.bytes) + 1)
+        self.xs = [x] + [x.clone() for _ in range(ncopy - 1)]
+        self.outs = []
+        for _ in range(ncopy):
+            if kind == "e4m3":
+                self.outs.append((torch.empty((rows, cols), dtype=torch.uint8, device="cuda"),
+                                  torch.empty((rows, cols // 128), dtype=torch.float32, device="cuda")))
+            else:
+                self.outs.append((torch.empty((rows, cols // 2), dtype=torch.uint8, device="cuda"),
+                                  torch.empty((rows, cols // 16), dtype=torch.uint8, device="cuda")))
+
+    def launch(self, i):
+        j = i % len(self.xs)
+        c, s = self.outs[j]
+        if self.kind == "e4m3":
+            self.W.quantize_e4m3(self.xs[j], 128, codes=c, scales=s)
+        else:
+            self.W.quantize_mxfp4(self.xs[j], 16, codes=c, scales=s)
+
+
+class WeightQuant:
+    """14336 x 4096 fp32 -> MXFP4 block 32 (offline weight preparation)."""
+
+    def __init__(self, torch, W):
+        from synthetic import prefill_inputs
+        self.W = W
+        _, Wf = prefill_inputs(0, with_x=False)
+        self.w = [torch.from_numpy(Wf).cuda()]
+        self.w.append(self.w[0].clone())
+        rows, cols = Wf.shape
+        self.bytes = rows * cols * 4 + rows * cols // 2 + rows * cols // 32
+        self.outs = [(torch.empty((rows, cols // 2), dtype=torch.uint8, device="cuda"),
+                      torch.empty((rows, cols // 32), dtype=torch.uint8, device="cuda")) for _ in range(2)]
+
+    def launch(self, i):
+        c, s = self.outs[i % 2]
+        self.W.quantize_mxfp4(self.w[i % 2], 32, codes=c, scales=s)
+
+
+class Copy:
+    """Streaming copy of 256 MiB (read + write) as a secondary HBM denominator."""
+
+    def __init__(self, torch):
+        n = 1 << 26
+        self.a = [torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0) for _ in range(3)]
+        self.b = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(3)]
+        self.bytes = 2 * n * 4
+
+    def launch(self, i):
+        self.b[i % 3].copy_(self.a[i % 3])
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the decode workload
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(rows=4096, reps=3):
+    from threadpoolctl import threadpool_limits
+    from oracle import dequant as OD
+    from oracle import gemm as OG
+    from oracle import int4 as OI
+    from synthetic import decode_inputs
+    xbits, Wf = decode_inputs(1, seed=0)
+    Wf = Wf[:rows]
+    packed, sb, _ = OI.quantize_int4(Wf, 128)          # weight preparation, not timed
+    K = Wf.shape[1]
+    nbytes = packed.nbytes + sb.nbytes + K * 2 + rows * 2
+    times = []
+    with threadpool_limits(limits=1):
+        for _ in range(reps):
+            t = time.perf_counter()
+            wd = OD.dequant_int4(packed, sb, 128)
+            y, _ = OG.reference(xbits, wd)
+            times.append(time.perf_counter() - t)
+    t = float(np.median(times))
+    return {"value": nbytes / t / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"decode W4A16 M=1 K=4096 on the first {rows} of 14336 output rows "
+                      f"(INT4 dequant + fp64 matvec), median of {reps}, single-threaded",
+            "seconds_per_sample_step": t}
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(no collective or sharded path is built).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import weight_only_quantized_quant_amd as W
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    if args.only:
+        case = args.only
+        mk = {"decode": lambda: Decode(torch, W, 1), "decode_w8": lambda: Decode(torch, W, 1, "e4m3"),
+              "prefill": lambda: Prefill(torch, W), "quant_e4m3": lambda: ActQuant(torch, W, "e4m3"),
+              "quant_mxfp4": lambda: ActQuant(torch, W, "mxfp4"), "copy": lambda: Copy(torch),
+              "wquant_mxfp4": lambda: WeightQuant(torch, W)}[case]
+        obj = mk()
+        reps = args.reps or (10 if case == "prefill" else 100)
+        for i in range(reps):
+            obj.launch(i)
+        torch.cuda.synchronize()
+        print(f"{case}: {reps} launches done", flush=True)
+        return
+
+    K, Wm = args.steps, args.warmup
+    dec = Decode(torch, W, 1)
+    warm_g = graph_of(torch, [lambda i=i: dec.launch(i) for i in range(max(1, Wm))])
+    timed_g = graph_of(torch, [lambda i=i: dec.launch(i) for i in range(K)])
+    warm_g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms = time_graph(torch, timed_g, K)
+    wall = time.perf_counter() - t0
+    value = dec.bytes / (ms * 1e-3) / 1e9
+    traffic = stored_traffic("decode_w4a16_m1", dec.bytes)
+    roofline = {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(value / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "k_gemv<INT4,TN=1> (wq_gemm, M<=16 path)",
+                "bytes_per_launch": dec.bytes, "us_per_launch": round(ms * 1e3, 3)}
+    del timed_g, warm_g
+
+    secondary = {}
+
+    def add_decode(label, M, kind):
+        d = Decode(torch, W, M, kind)
+        g = graph_of(torch, [lambda i=i: d.launch(i) for i in range(100)])
+        g.replay()
+        t = time_graph(torch, g, 100)
+        secondary[label] = {"GB/s": round(d.bytes / (t * 1e-3) / 1e9, 1), "us": round(t * 1e3, 3),
+                            "frac_hbm": round(d.bytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bytes": d.bytes}
+        del g, d
+
+    add_decode("decode_w4a16_m4", 4, "int4")
+    add_decode("decode_w4a16_m16", 16, "int4")
+    add_decode("decode_w8a16_m1", 1, "e4m3")
+    torch.cuda.empty_cache()
+
+    pf = Prefill(torch, W)
+    t = time_eager(torch, pf.launch, 10)
+    tf = pf.flops / (t * 1e-3) / 1e12
+    secondary["prefill_mxfp4_m8192"] = {"TFLOP/s": round(tf, 1), "frac_bf16_mfma": round(tf / BF16_PEAK_TFLOPS, 4),
+                                        "ms": round(t, 3), "flops": pf.flops}
+    # secondary denominator: torch.matmul bf16 (hipBLASLt) at the same shape
+    wb = torch.empty((pf.N, pf.K), dtype=torch.bfloat16, device="cuda").normal_()
+    t2 = time_eager(torch, lambda i: torch.matmul(pf.x, wb.t()), 10)
+    secondary["torch_matmul_bf16_8192x14336x4096"] = {"TFLOP/s": round(pf.flops / (t2 * 1e-3) / 1e12, 1),
+                                                      "ms": round(t2, 3)}
+    del pf, wb
+    torch.cuda.empty_cache()
+
+    for kind in ("e4m3", "mxfp4"):
+        q = ActQuant(torch, W, kind)
+        g = graph_of(torch, [lambda i=i: q.launch(i) for i in range(40)])
+        g.replay()
+        t = time_graph(torch, g, 40)
+        secondary[f"act_quant_{kind}_4096x7168"] = {"GB/s": round(q.bytes / (t * 1e-3) / 1e9, 1),
+                                                    "us": round(t * 1e3, 2),
+                                                    "frac_hbm": round(q.bytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del g, q
+    wq_ = WeightQuant(torch, W)
+    t = time_eager(torch, wq_.launch, 10)
+    secondary["weight_quant_mxfp4_14336x4096_fp32"] = {"GB/s": round(wq_.bytes / (t * 1e-3) / 1e9, 1),
+                                                       "us": round(t * 1e3, 2)}
+    del wq_
+    cp = Copy(torch)
+    t = time_eager(torch, cp.launch, 20)
+    secondary["stream_copy_256MiB"] = {"GB/s": round(cp.bytes / (t * 1e-3) / 1e9, 1)}
+    del cp
+    torch.cuda.empty_cache()
+
+    cpu = None if args.no_cpu else cpu_baseline()
+
+    line = {
+        "metric": "wq_gemm decode GB/s (% HBM peak) at M=1; prefill TFLOP/s (% bf16 MFMA peak)",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": Wm,
+        "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "decode W4A16 GEMV: M=1, K=4096, N=14336, INT4 (8 per uint32) with bf16 scales "
+                               "per 128-element group; bf16 x with 0.5% channels x30; weights cycled over "
+                               f"{len(dec.copies)} resident copies", "parallelism": "none (1 GPU)"},
+        "roofline": roofline, "cpu_baseline": cpu, "secondary": secondary,
+        "wall_s_timed_region": round(wall, 4),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

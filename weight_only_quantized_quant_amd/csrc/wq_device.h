@@ -68,44 +68,31 @@ __device__ __forceinline__ uint32_t e8m0_code(float vmax) {
 // INT4 dequantization of one packed word (8 two's-complement nibbles) with
 // bf16-valued group scale s: out[i] holds bf16(q_2i * s), bf16(q_2i+1 * s).
 //
-// Each nibble n is placed in the mantissa of a float with unit exponent,
-// f = 1 + u * 2^(p-23) with u = n ^ 8 = q + 8 the offset-binary nibble at bit
-// position p in {8, 12, 16}; then fma(f, s * 2^(23-p), -(2^(23-p) + 8) * s)
-// equals (u - 8) * s = q * s exactly (both constants are exact fp32 numbers
-// because s has 8 significant bits), and one RNE conversion makes bf16(q*s).
-struct Int4Consts {
-  float a8, b8, a12, b12, a16, b16;
-};
-__device__ __forceinline__ Int4Consts int4_consts(float s) {
-  Int4Consts c;
-  c.a8 = s * 32768.0f;  c.b8 = s * -32776.0f;
-  c.a12 = s * 2048.0f;  c.b12 = s * -2056.0f;
-  c.a16 = s * 128.0f;   c.b16 = s * -136.0f;
-  return c;
-}
-__device__ __forceinline__ float int4_elem(uint32_t src, uint32_t mask, float a, float b) {
-  return __builtin_fmaf(__uint_as_float((src & mask) | 0x3F800000u), a, b);
-}
-__device__ __forceinline__ void dq_int4_word(uint32_t w, const Int4Consts& c, uint32_t out[4]) {
-  const uint32_t u = w ^ 0x88888888u;
-  const uint32_t lo = u << 8;    // nibbles 0,1 -> bit positions 8,12
-  const uint32_t hi = u >> 12;   // nibbles 5,6,7 -> bit positions 8,12,16
-  const float e0 = int4_elem(lo, 0xF00u, c.a8, c.b8);
-  const float e1 = int4_elem(lo, 0xF000u, c.a12, c.b12);
-  const float e2 = int4_elem(u, 0xF00u, c.a8, c.b8);
-  const float e3 = int4_elem(u, 0xF000u, c.a12, c.b12);
-  const float e4 = int4_elem(u, 0xF0000u, c.a16, c.b16);
-  const float e5 = int4_elem(hi, 0xF00u, c.a8, c.b8);
-  const float e6 = int4_elem(hi, 0xF000u, c.a12, c.b12);
-  const float e7 = int4_elem(hi, 0xF0000u, c.a16, c.b16);
-  out[0] = pack_bf16x2(e0, e1);
-  out[1] = pack_bf16x2(e2, e3);
-  out[2] = pack_bf16x2(e4, e5);
-  out[3] = pack_bf16x2(e6, e7);
+// Two v_bitop3_b32 split the word into bytes holding u = n ^ 8 = q + 8 (the
+// offset-binary nibble): ((w & 0x0F0F0F0F) ^ 0x08080808) for the even
+// nibbles, the same on w >> 4 for the odd ones.  v_cvt_f32_ubyte{0..3} turn a
+// byte into an exact float, fma(u, s, -8 s) = (u - 8) * s = q * s is exact
+// (-8 s is exact and q * s has at most 11 significant bits), and one RNE
+// conversion per pair makes bf16(q * s).  Exact in value for 0 < s <= 2^120;
+// for s <= 0 a zero product may come out as +0 instead of -0.
+__device__ __forceinline__ void dq_int4_word(uint32_t w, float s, uint32_t out[4]) {
+  // truth table of (S0 & S1) ^ S2 with S0 = 0xF0, S1 = 0xCC, S2 = 0xAA
+  constexpr uint8_t AND_XOR = (uint8_t)((0xF0 & 0xCC) ^ 0xAA);
+  const uint32_t ue = __builtin_amdgcn_bitop3_b32(w, 0x0F0F0F0Fu, 0x08080808u, AND_XOR);
+  const uint32_t uo = __builtin_amdgcn_bitop3_b32(w >> 4, 0x0F0F0F0Fu, 0x08080808u, AND_XOR);
+  const float b = s * -8.0f;
+  float e[8];
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    e[2 * j] = __builtin_fmaf((float)((ue >> (8 * j)) & 0xFFu), s, b);
+    e[2 * j + 1] = __builtin_fmaf((float)((uo >> (8 * j)) & 0xFFu), s, b);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; j++) out[j] = pack_bf16x2(e[2 * j], e[2 * j + 1]);
 }
 
 // Same result for any finite s: the magic-constant route above needs
-// s * 2^15 to stay finite, and for s <= 0 it would give +0 where q * s is -0,
+// 15 * s to stay finite, and for s <= 0 it would give +0 where q * s is -0,
 // so those scales take the direct route (sign-extend each nibble, exact fp32
 // product q * s, one RNE conversion).
 __device__ __forceinline__ void dq_int4_word_direct(uint32_t w, float s, uint32_t out[4]) {
@@ -115,7 +102,7 @@ __device__ __forceinline__ void dq_int4_word_direct(uint32_t w, float s, uint32_
 #pragma unroll
   for (int j = 0; j < 4; j++) out[j] = pack_bf16x2(e[2 * j], e[2 * j + 1]);
 }
-__device__ __forceinline__ bool int4_scale_fast(float s) { return s > 0.0f && s <= 0x1p100f; }
+__device__ __forceinline__ bool int4_scale_fast(float s) { return s > 0.0f && s <= 0x1p120f; }
 
 // E2M1 word (8 codes) with E8M0 scale operand -> 4 bf16 pairs.
 __device__ __forceinline__ void dq_fp4_word(uint32_t w, float sc, uint32_t out[4]) {

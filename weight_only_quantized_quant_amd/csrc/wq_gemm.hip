@@ -50,21 +50,11 @@ __device__ __forceinline__ float load_scale(const void* sc, int64_t row, int64_t
 template <int WDT>
 __device__ __forceinline__ void dequant16(u32x4_t w, float s, bf16x8_t out[4]) {
   if constexpr (WDT == W_INT4) {
-    if (int4_scale_fast(s)) {
-      const Int4Consts c = int4_consts(s);
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
-        uint32_t o[4];
-        dq_int4_word(w[j], c, o);
-        out[j] = as_bf16x8(o[0], o[1], o[2], o[3]);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        uint32_t o[4];
-        dq_int4_word_direct(w[j], s, o);
-        out[j] = as_bf16x8(o[0], o[1], o[2], o[3]);
-      }
+    for (int j = 0; j < 4; j++) {
+      uint32_t o[4];
+      dq_int4_word(w[j], s, o);
+      out[j] = as_bf16x8(o[0], o[1], o[2], o[3]);
     }
   } else if constexpr (WDT == W_FP4) {
 #pragma unroll
@@ -85,60 +75,113 @@ __device__ __forceinline__ void dequant16(u32x4_t w, float s, bf16x8_t out[4]) {
 // ---------------------------------------------------------------------------
 // Decode GEMV
 // ---------------------------------------------------------------------------
-template <int WDT, int TN, int CH>
+// Raw buffer resources: loads past `bytes` return zeros, which pads the rows
+// beyond N and the x rows beyond M without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int64_t lim = bytes < 0 ? 0 : (bytes > 0x7FFFFFF0LL ? 0x7FFFFFF0LL : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)lim, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t bld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+template <int WDT>
+__device__ __forceinline__ float scale_of(__amdgpu_buffer_rsrc_t r, uint32_t idx) {
+  if constexpr (WDT == W_INT4) return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, (int)(idx * 2), 0, 0));
+  else if constexpr (WDT == W_FP4) return e8m0_as_scale(__builtin_amdgcn_raw_buffer_load_b8(r, (int)idx, 0, 0));
+  else return 1.0f;
+}
+
+// XLDS (M <= 4): each wave stages the x rows of its own K chunk in a private
+// LDS region (M x NSTEP*KSTEP bf16, one 16-byte load per lane per row) next to
+// a 64-byte zero block; lanes whose MFMA row is >= M read the zero block.
+// No workgroup barrier is needed: LDS operations of one wave execute in order.
+// Otherwise x is read with buffer loads (rows >= M read as zeros).
+// Issue order per chunk: x staging loads, scales, weights.
+template <int WDT, int TN, int NSTEP, bool XLDS>
 __global__ __launch_bounds__(512) void k_gemv(const uint16_t* __restrict__ x, int M, int64_t N, int64_t K,
-                                             const uint8_t* __restrict__ w, const void* __restrict__ sc, int group,
-                                             const float* __restrict__ chscale, uint16_t* __restrict__ y, int kw) {
+                                             const uint8_t* __restrict__ w, const void* __restrict__ sc,
+                                             int group_shift, const float* __restrict__ chscale,
+                                             uint16_t* __restrict__ y, int niter) {
   constexpr int EPL = WTraits<WDT>::bits == 4 ? 32 : 16;   // elements per lane per step
   constexpr int KSTEP = 4 * EPL;                            // K covered by a wave per step
+  constexpr int KCH = NSTEP * KSTEP;                        // K per wave per chunk
   constexpr int MF = EPL / 8;                               // MFMAs per step per tile
   constexpr int BPE2 = WTraits<WDT>::bits == 4 ? 1 : 2;     // bytes per 2 elements
-  extern __shared__ float red[];                            // [S][TN][16][16]
+  constexpr int SB = WDT == W_INT4 ? 2 : 1;                 // bytes per scale
+  constexpr int XW = 4 * KCH * 2 + 64;                      // per-wave x region (up to 4 rows)
+  static_assert(KCH == 512 || !XLDS || KCH < 512, "x staging uses one 16-byte chunk per lane per 512 k");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int S = blockDim.x >> 6;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nl = lane & 15, g = lane >> 4;
   const int64_t n0 = (int64_t)blockIdx.x * 16 * TN;
-  const int64_t kbeg = (int64_t)wave * kw, kend = kbeg + kw;
-  const int64_t rowbytes = K * BPE2 / 2;
+  const uint32_t rowbytes = (uint32_t)(K * BPE2 / 2);
+  const int64_t nrows = N - n0 < 16 * TN ? N - n0 : 16 * TN;
+  const int gs = WDT == W_INT4 ? group_shift : 5;            // log2 of the scale group
+  const uint32_t spr = (uint32_t)(K >> gs);                  // scales per row
+  const auto rw = make_rsrc(w + n0 * rowbytes, nrows * rowbytes);
+  const auto rs = make_rsrc(reinterpret_cast<const uint8_t*>(sc) + (WDT == W_FP8 ? 0 : n0 * spr * SB),
+                            WDT == W_FP8 ? 0 : nrows * spr * SB);
+  const auto rx = make_rsrc(x, (int64_t)M * K * 2);
+  const uint32_t kbase = (uint32_t)(wave * niter * KCH);
 
-  int64_t nrow[TN];
-#pragma unroll
-  for (int t = 0; t < TN; t++) {
-    const int64_t n = n0 + 16 * t + nl;
-    nrow[t] = n < N ? n : N - 1;                 // clamped: always a valid row
+  uint8_t* xw = smem + wave * XW;                            // this wave's x rows, then zeros
+  float* red = reinterpret_cast<float*>(smem + (XLDS ? S * XW : 0));
+  if constexpr (XLDS) {
+    if (lane < 4) *reinterpret_cast<u32x4_t*>(xw + 4 * KCH * 2 + 16 * lane) = u32x4_t{0u, 0u, 0u, 0u};
   }
-  const bool xrow = nl < M;                      // this lane carries a real x row
-  const uint16_t* xr = x + (int64_t)(xrow ? nl : 0) * K;
 
   f32x4_t acc[TN];
 #pragma unroll
   for (int t = 0; t < TN; t++) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t k0 = kbeg; k0 < kend; k0 += (int64_t)CH * KSTEP) {
-    u32x4_t wr[CH][TN];
-    float sv[CH][TN];
+  for (int it = 0; it < niter; it++) {
+    const uint32_t k0 = kbase + (uint32_t)(it * KCH);
+    // x staging: row r, 16-byte chunk `lane` of the KCH-wide slice (KCH/8 chunks <= 64)
+    u32x4_t xst[4];
+    if constexpr (XLDS) {
 #pragma unroll
-    for (int c = 0; c < CH; c++) {
-      const int64_t kk = k0 + (int64_t)c * KSTEP + (int64_t)EPL * g;
-      if (k0 + (int64_t)c * KSTEP < kend) {
+      for (int r = 0; r < 4; r++)
+        if (r < M && lane < KCH / 8) xst[r] = bld16(rx, (uint32_t)(r * (uint32_t)K + k0 + 8 * lane) * 2);
+    }
+    float sv[NSTEP][TN];
+    u32x4_t wr[NSTEP][TN];
 #pragma unroll
-        for (int t = 0; t < TN; t++) {
-          wr[c][t] = ld16(w + nrow[t] * rowbytes + kk * BPE2 / 2);
-          sv[c][t] = load_scale<WDT>(sc, nrow[t], K, group, kk);
-        }
+    for (int c = 0; c < NSTEP; c++)
+#pragma unroll
+      for (int t = 0; t < TN; t++) {
+        const uint32_t kk = k0 + c * KSTEP + EPL * g;
+        sv[c][t] = scale_of<WDT>(rs, (uint32_t)(16 * t + nl) * spr + (kk >> gs));
       }
+#pragma unroll
+    for (int c = 0; c < NSTEP; c++)
+#pragma unroll
+      for (int t = 0; t < TN; t++) {
+        const uint32_t kk = k0 + c * KSTEP + EPL * g;
+        wr[c][t] = bld16(rw, (uint32_t)(16 * t + nl) * rowbytes + kk * BPE2 / 2);
+      }
+    if constexpr (XLDS) {
+#pragma unroll
+      for (int r = 0; r < 4; r++)
+        if (r < M && lane < KCH / 8) *reinterpret_cast<u32x4_t*>(xw + (r * KCH + 8 * lane) * 2) = xst[r];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 #pragma unroll
-    for (int c = 0; c < CH; c++) {
-      if (k0 + (int64_t)c * KSTEP >= kend) break;
-      const int64_t kk = k0 + (int64_t)c * KSTEP + (int64_t)EPL * g;
+    for (int c = 0; c < NSTEP; c++) {
       bf16x8_t xa[MF];
 #pragma unroll
       for (int j = 0; j < MF; j++) {
-        u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-        if (xrow) v = ld16(xr + kk + 8 * j);
-        xa[j] = as_bf16x8(v);
+        const uint32_t kl = c * KSTEP + EPL * g + 8 * j;       // k within the chunk
+        if constexpr (XLDS) {
+          const uint32_t off = nl < M ? (nl * KCH + kl) * 2 : 4 * KCH * 2;
+          xa[j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(xw + off));
+        } else {
+          xa[j] = as_bf16x8(bld16(rx, (nl * (uint32_t)K + k0 + kl) * 2));
+        }
       }
 #pragma unroll
       for (int t = 0; t < TN; t++) {
@@ -147,6 +190,12 @@ __global__ __launch_bounds__(512) void k_gemv(const uint16_t* __restrict__ x, in
 #pragma unroll
         for (int j = 0; j < MF; j++) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[j], b[j], acc[t], 0, 0, 0);
       }
+    }
+    if constexpr (XLDS) {
+      // the next chunk's staging overwrites this wave's region
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   }
 
@@ -327,24 +376,245 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ x, in
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode GEMV, LDS-ring form (M <= 4)
+// ---------------------------------------------------------------------------
+// A workgroup of 4 waves owns 16 output columns; wave w owns the K-slice of
+// SPW steps [w*SPW, (w+1)*SPW).  Packed weights never occupy VGPRs while in
+// flight: each step's 16 rows x 64 bytes (1 KB) are fetched by direct-to-LDS
+// buffer loads into one of R ring slots of the wave, so many steps of every
+// wave are outstanding at once.  Lane l fetches, and later reads back, the 16
+// bytes it feeds to the MFMA (row l % 16, K offset 32 or 16 elements times
+// l / 16), so the LDS ring needs no cross-lane synchronisation.  The x rows of
+// the slice are fetched the same way once.  MFMA rows >= M read row 0 of x;
+// those output rows are discarded.
+
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, (int)voff, 0,
+                                           0, 0);
+}
+// s_waitcnt with vmcnt <= n, other counters unconstrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int WDT, int SPW, int R, int NW>
+__global__ __launch_bounds__(64 * NW) void k_gemv_ring(const uint16_t* __restrict__ x, int M, int64_t N, int64_t K,
+                                                  const uint8_t* __restrict__ w, const void* __restrict__ sc,
+                                                  int group_shift, const float* __restrict__ chscale,
+                                                  uint16_t* __restrict__ y) {
+  constexpr int EPL = WTraits<WDT>::bits == 4 ? 32 : 16;
+  constexpr int KSTEP = 4 * EPL;
+  constexpr int KSL = SPW * KSTEP;                            // K of one wave's slice
+  constexpr int MF = EPL / 8;
+  constexpr int BPE2 = WTraits<WDT>::bits == 4 ? 1 : 2;
+  constexpr int XROW = KSL * 2;                               // bytes of one x row of the slice
+  static_assert(R <= SPW, "ring larger than the slice");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nl = lane & 15, g = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const uint32_t rowbytes = (uint32_t)(K * BPE2 / 2);
+  const int64_t nrows = N - n0 < 16 ? N - n0 : 16;
+  const int gs = WDT == W_INT4 ? group_shift : 5;
+  const uint32_t spr = (uint32_t)(K >> gs);                  // scales per row
+  constexpr int SB = WDT == W_INT4 ? 2 : 1;                   // bytes per scale
+  const uint32_t sbrow = (uint32_t)(KSL >> gs) * SB;         // scale bytes per row of the slice
+  const auto rw = make_rsrc(w + n0 * rowbytes, nrows * rowbytes);
+  const auto rs = make_rsrc(reinterpret_cast<const uint8_t*>(sc) + (WDT == W_FP8 ? 0 : n0 * spr * SB),
+                            WDT == W_FP8 ? 0 : nrows * spr * SB);
+  const auto rx = make_rsrc(x, (int64_t)M * K * 2);
+  const uint32_t kbase = (uint32_t)(wave * KSL);
+  // per-wave LDS: ring | M x rows | scales of the slice (16 rows, row stride srs)
+  const uint32_t srs = sbrow < 16 ? 16 : sbrow;
+  const int sbytes = WDT == W_FP8 ? 0 : 16 * (int)srs;
+  const int wstride = R * 1024 + M * XROW + ((sbytes + 15) & ~15);
+  uint8_t* ring = smem + wave * wstride;
+  uint8_t* xl = ring + R * 1024;
+  uint8_t* sl = xl + M * XROW;
+
+  // 1) scales of the slice.  When a row of the slice holds >= 16 bytes of
+  //    scales (a multiple of 16), they arrive by DMA, 16 bytes per lane; for
+  //    thinner slices every lane loads its own per-step scales instead (a 16-byte
+  //    window could leave the buffer range at the last row and read as zeros).
+  const bool sdma = sbrow >= 16;
+  float svr[SPW];
+  if constexpr (WDT != W_FP8) {
+    if (sdma) {
+      const int cpr = (int)srs / 16;
+      if (lane < 16 * cpr)
+        lds_dma16(rs, sl, (uint32_t)(lane / cpr) * spr * SB + (kbase >> gs) * SB + 16 * (lane % cpr));
+    } else {
+#pragma unroll
+      for (int c = 0; c < SPW; c++)
+        svr[c] = scale_of<WDT>(rs, (uint32_t)nl * spr + ((kbase + c * KSTEP + EPL * g) >> gs));
+    }
+  }
+  // 2) x rows of the slice, 1 KB per DMA instruction
+#pragma unroll
+  for (int r = 0; r < 4; r++)
+    if (r < M)
+#pragma unroll
+      for (int q = 0; q < (XROW + 1023) / 1024; q++)
+        if (q * 1024 + lane * 16 < XROW)
+          lds_dma16(rx, xl + r * XROW + q * 1024, (uint32_t)(r * (uint32_t)K + kbase + q * 512 + 8 * lane) * 2);
+  // 3) the first R weight steps
+  const uint32_t wlane = (uint32_t)nl * rowbytes + (kbase + EPL * g) * BPE2 / 2;
+#pragma unroll
+  for (int c = 0; c < R; c++) lds_dma16(rw, ring + c * 1024, wlane + c * KSTEP * BPE2 / 2);
+
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int xr = nl < M ? nl : 0;
+#pragma unroll
+  for (int c = 0; c < SPW; c++) {
+    // weight loads issued after step c's: min(R-1, SPW-1-c) (refills are issued in step order)
+    if (c + R - 1 < SPW) wait_vm<R - 1>();
+    else {
+      switch (SPW - 1 - c) {
+        case 0: wait_vm<0>(); break;
+        case 1: wait_vm<1>(); break;
+        case 2: wait_vm<2>(); break;
+        case 3: wait_vm<3>(); break;
+        case 4: wait_vm<4>(); break;
+        case 5: wait_vm<5>(); break;
+        case 6: wait_vm<6>(); break;
+        default: wait_vm<0>(); break;
+      }
+    }
+    const u32x4_t wv = *reinterpret_cast<const u32x4_t*>(ring + (c % R) * 1024 + lane * 16);
+    float scv = 1.0f;
+    if constexpr (WDT == W_INT4) {
+      const uint32_t gi = (uint32_t)(c * KSTEP + EPL * g) >> gs;
+      scv = sdma ? bf16_to_f32(*reinterpret_cast<const uint16_t*>(sl + nl * srs + 2 * gi)) : svr[c];
+    } else if constexpr (WDT == W_FP4) {
+      const uint32_t gi = (uint32_t)(c * KSTEP + EPL * g) >> 5;
+      scv = sdma ? e8m0_as_scale(sl[nl * srs + gi]) : svr[c];
+    }
+    bf16x8_t xa[MF];
+#pragma unroll
+    for (int j = 0; j < MF; j++)
+      xa[j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(xl + xr * XROW + (c * KSTEP + EPL * g + 8 * j) * 2));
+    bf16x8_t b[4];
+    dequant16<WDT>(wv, scv, b);
+    // the slot's bytes are consumed (in registers): refill it with step c + R
+    if (c + R < SPW) lds_dma16(rw, ring + (c % R) * 1024, wlane + (c + R) * KSTEP * BPE2 / 2);
+#pragma unroll
+    for (int j = 0; j < MF; j++) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[j], b[j], acc, 0, 0, 0);
+  }
+
+  // split-K reduction in the (consumed) front of the workgroup's LDS
+  float* red = reinterpret_cast<float*>(smem);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; i++) red[(wave * 16 + 4 * g + i) * 16 + nl] = acc[i];
+  __syncthreads();
+  if (threadIdx.x < 256) {
+    const int m = threadIdx.x >> 4, n = threadIdx.x & 15;
+    const int64_t col = n0 + n;
+    if (m < M && col < N) {
+      float s = 0.0f;
+#pragma unroll
+      for (int wv = 0; wv < NW; wv++) s += red[(wv * 16 + m) * 16 + n];
+      if constexpr (WDT == W_FP8) s *= chscale[col];
+      y[(int64_t)m * N + col] = (uint16_t)f32_to_bf16_bits(s);
+    }
+  }
+}
+
+// Split of the K loop: T = K / KSTEP steps = S waves x niter iterations x NSTEP.
+struct GemvSplit { int nstep, S, niter; };
+inline GemvSplit gemv_split(int64_t T, int maxstep) {
+  for (int ns = maxstep; ns >= 1; ns >>= 1) {
+    if (T % ns) continue;
+    const int64_t steps = T / ns;
+    for (int S = 8; S >= 1; S--)
+      if (steps % S == 0) return GemvSplit{ns, S, (int)(steps / S)};
+  }
+  return GemvSplit{1, 1, (int)T};
+}
+
+template <int WDT, int TN, int NSTEP, bool XLDS>
+void gemv_go(const GemvSplit& sp, const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w,
+             const void* sc, int group, const float* ch, uint16_t* y, hipStream_t s) {
+  const unsigned grid = (unsigned)((N + 16 * TN - 1) / (16 * TN));
+  constexpr int KCH = NSTEP * (WTraits<WDT>::bits == 4 ? 128 : 64);
+  const size_t lds = (XLDS ? (size_t)sp.S * (4 * KCH * 2 + 64) : 0) + (size_t)sp.S * TN * 1024;
+  const int gshift = group == 32 ? 5 : group == 64 ? 6 : 7;
+  k_gemv<WDT, TN, NSTEP, XLDS><<<grid, 64 * sp.S, lds, s>>>(x, (int)M, N, K, w, sc, gshift, ch, y, sp.niter);
+}
+
+template <int WDT, int TN, bool XLDS>
+void gemv_nstep(const GemvSplit& sp, const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w,
+                const void* sc, int group, const float* ch, uint16_t* y, hipStream_t s) {
+  switch (sp.nstep) {
+    case 8: if constexpr (WTraits<WDT>::bits == 8) { gemv_go<WDT, TN, 8, XLDS>(sp, x, M, N, K, w, sc, group, ch, y, s); break; }
+            [[fallthrough]];
+    case 4: gemv_go<WDT, TN, 4, XLDS>(sp, x, M, N, K, w, sc, group, ch, y, s); break;
+    case 2: gemv_go<WDT, TN, 2, XLDS>(sp, x, M, N, K, w, sc, group, ch, y, s); break;
+    default: gemv_go<WDT, TN, 1, XLDS>(sp, x, M, N, K, w, sc, group, ch, y, s); break;
+  }
+}
+
+#ifndef WQ_RING_DEPTH
+#define WQ_RING_DEPTH 8
+#endif
+#ifndef WQ_RING_WAVES
+#define WQ_RING_WAVES 4
+#endif
+constexpr int RING_NW = WQ_RING_WAVES;
+template <int WDT, int SPW>
+void ring_go(int64_t M, const uint16_t* x, int64_t N, int64_t K, const uint8_t* w, const void* sc, int gshift,
+             const float* ch, uint16_t* y, hipStream_t s) {
+  constexpr int R0 = SPW < WQ_RING_DEPTH ? SPW : WQ_RING_DEPTH;
+  constexpr int KSL = SPW * (WTraits<WDT>::bits == 4 ? 128 : 64);
+  const int gs = WDT == W_INT4 ? gshift : 5;
+  const int sbrow = (KSL >> gs) * (WDT == W_INT4 ? 2 : 1);
+  const int sbytes = WDT == W_FP8 ? 0 : 16 * (sbrow < 16 ? 16 : sbrow);
+  const unsigned grid = (unsigned)((N + 15) / 16);
+  auto lds_for = [&](int r) { return (size_t)RING_NW * (r * 1024 + M * KSL * 2 + ((sbytes + 15) & ~15)); };
+  // 4 resident 4-wave workgroups per CU need <= 40 KB each; trade ring depth for it
+  const size_t budget = (size_t)160 * 1024 * RING_NW / 16;
+  if (R0 >= 7 && lds_for(R0) > budget && lds_for(R0 - 1) <= budget) {
+    constexpr int R = R0 >= 7 ? R0 - 1 : R0;
+    k_gemv_ring<WDT, SPW, R, RING_NW><<<grid, 64 * RING_NW, lds_for(R), s>>>(x, (int)M, N, K, w, sc, gshift, ch, y);
+  } else {
+    k_gemv_ring<WDT, SPW, R0, RING_NW><<<grid, 64 * RING_NW, lds_for(R0), s>>>(x, (int)M, N, K, w, sc, gshift, ch, y);
+  }
+}
+
 template <int WDT>
 wq_status launch_gemv(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w, const void* sc, int group,
                       const float* ch, uint16_t* y, hipStream_t s) {
   constexpr int KSTEP = WTraits<WDT>::bits == 4 ? 128 : 64;
-  constexpr int CH = WTraits<WDT>::bits == 4 ? 4 : 8;
-  int S = 8;
-  while (S > 1 && (K % ((int64_t)S * KSTEP) != 0)) S >>= 1;
-  if (K % ((int64_t)S * KSTEP) != 0) return WQ_EINVAL;
-  const int kw = (int)(K / S);
-  if (M <= 4) {
-    constexpr int TN = 1;
-    const unsigned grid = (unsigned)((N + 16 * TN - 1) / (16 * TN));
-    k_gemv<WDT, TN, CH><<<grid, 64 * S, S * TN * 1024, s>>>(x, (int)M, N, K, w, sc, group, ch, y, kw);
-  } else {
-    constexpr int TN = 2;
-    const unsigned grid = (unsigned)((N + 16 * TN - 1) / (16 * TN));
-    k_gemv<WDT, TN, CH><<<grid, 64 * S, S * TN * 1024, s>>>(x, (int)M, N, K, w, sc, group, ch, y, kw);
+  const int gshift = group == 32 ? 5 : group == 64 ? 6 : 7;
+  if (M <= 4 && K % (KSTEP * RING_NW) == 0 && 16 * K * 2 <= 0x7FFFFFF0LL) {
+    const int64_t spw = K / (KSTEP * RING_NW);
+    if (spw == 1 || spw == 2 || spw == 4 || spw == 8 || spw == 16) {
+      switch (spw) {
+        case 1: ring_go<WDT, 1>(M, x, N, K, w, sc, gshift, ch, y, s); break;
+        case 2: ring_go<WDT, 2>(M, x, N, K, w, sc, gshift, ch, y, s); break;
+        case 4: ring_go<WDT, 4>(M, x, N, K, w, sc, gshift, ch, y, s); break;
+        case 8: ring_go<WDT, 8>(M, x, N, K, w, sc, gshift, ch, y, s); break;
+        default: ring_go<WDT, 16>(M, x, N, K, w, sc, gshift, ch, y, s); break;
+      }
+      return wq_launch_status();
+    }
   }
+  constexpr int MAXSTEP = WTraits<WDT>::bits == 4 ? 4 : 8;
+  // the per-workgroup buffer resources address 16*TN rows (< 2^31 bytes)
+  if (32 * K * (WTraits<WDT>::bits / 4) / 2 > 0x7FFFFFF0LL || M * K * 2 > 0x7FFFFFF0LL) return WQ_EINVAL;
+  if (K % KSTEP) {
+    // K = 128*j with j odd only matters for 8-bit weights, whose step is 64: always divisible
+    return WQ_EINVAL;
+  }
+  const GemvSplit sp = gemv_split(K / KSTEP, MAXSTEP);
+  const bool xlds = M <= 4;
+  if (xlds) gemv_nstep<WDT, 1, true>(sp, x, M, N, K, w, sc, group, ch, y, s);
+  else if (M <= 4) gemv_nstep<WDT, 1, false>(sp, x, M, N, K, w, sc, group, ch, y, s);
+  else gemv_nstep<WDT, 2, false>(sp, x, M, N, K, w, sc, group, ch, y, s);
   return wq_launch_status();
 }
 

@@ -193,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void k_dq_int4(const uint32_t* __restrict
   const int64_t e = t * 8, n = e / K, k = e % K;
   const float s = bf16_to_f32(scales[n * (K / group) + k / group]);
   uint32_t o[4];
-  if (int4_scale_fast(s)) dq_int4_word(packed[t], int4_consts(s), o);
+  if (int4_scale_fast(s)) dq_int4_word(packed[t], s, o);
   else dq_int4_word_direct(packed[t], s, o);
   *reinterpret_cast<u32x4_t*>(out + e) = u32x4_t{o[0], o[1], o[2], o[3]};
 }
