@@ -19,8 +19,9 @@ M = 8192 (TFLOP/s), the activation quantizers at 4096 x 7168, the MXFP4 weight
 quantizer, a streaming copy and torch.matmul (hipBLASLt) at the prefill shape
 as secondary denominators.
 
---only CASE runs a single case without the JSON summary (for rocprofv3):
-decode, decode_w8, prefill, quant_e4m3, quant_mxfp4, copy.
+--only CASE runs a single case without the full summary (for rocprofv3):
+decode (the same graph-timed steps as the headline, prints one short JSON
+line), decode_w8, prefill, quant_e4m3, quant_mxfp4, wquant_mxfp4, copy.
 """
 from __future__ import annotations
 
@@ -289,9 +290,10 @@ def main():
     import weight_only_quantized_quant_amd as W
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
-    if args.only:
+    K, Wm = args.steps, args.warmup
+    if args.only and args.only != "decode":
         case = args.only
-        mk = {"decode": lambda: Decode(torch, W, 1), "decode_w8": lambda: Decode(torch, W, 1, "e4m3"),
+        mk = {"decode_w8": lambda: Decode(torch, W, 1, "e4m3"),
               "prefill": lambda: Prefill(torch, W), "quant_e4m3": lambda: ActQuant(torch, W, "e4m3"),
               "quant_mxfp4": lambda: ActQuant(torch, W, "mxfp4"), "copy": lambda: Copy(torch),
               "wquant_mxfp4": lambda: WeightQuant(torch, W)}[case]
@@ -303,7 +305,6 @@ def main():
         print(f"{case}: {reps} launches done", flush=True)
         return
 
-    K, Wm = args.steps, args.warmup
     dec = Decode(torch, W, 1)
     warm_g = graph_of(torch, [lambda i=i: dec.launch(i) for i in range(max(1, Wm))])
     timed_g = graph_of(torch, [lambda i=i: dec.launch(i) for i in range(K)])
@@ -316,9 +317,13 @@ def main():
     traffic = stored_traffic("decode_w4a16_m1", dec.bytes)
     roofline = {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(value / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "k_gemv<INT4,TN=1> (wq_gemm, M<=16 path)",
+                "kernel": "k_gemv_ring<INT4> (wq_gemm, M<=4 decode path)",
                 "bytes_per_launch": dec.bytes, "us_per_launch": round(ms * 1e3, 3)}
     del timed_g, warm_g
+    if args.only == "decode":
+        print(json.dumps({"case": "decode", "us_per_launch": roofline["us_per_launch"], "GB/s": roofline["achieved"],
+                          "launches_timed": K, "warmup": Wm}), flush=True)
+        return
 
     secondary = {}
 

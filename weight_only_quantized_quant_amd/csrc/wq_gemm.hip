@@ -558,17 +558,15 @@ void gemv_nstep(const GemvSplit& sp, const uint16_t* x, int64_t M, int64_t N, in
   }
 }
 
-#ifndef WQ_RING_DEPTH
-#define WQ_RING_DEPTH 8
-#endif
-#ifndef WQ_RING_WAVES
-#define WQ_RING_WAVES 4
-#endif
-constexpr int RING_NW = WQ_RING_WAVES;
+// Measured on MI355X for K = 4096: 4 waves per 16-column tile with a 2-deep
+// ring beat deeper rings (requests all in flight arrive in an order that
+// bunches the dequantization work at the end) and 8-wave splits.
+constexpr int RING_NW = 4;
+constexpr int RING_DEPTH = 2;
 template <int WDT, int SPW>
 void ring_go(int64_t M, const uint16_t* x, int64_t N, int64_t K, const uint8_t* w, const void* sc, int gshift,
              const float* ch, uint16_t* y, hipStream_t s) {
-  constexpr int R0 = SPW < WQ_RING_DEPTH ? SPW : WQ_RING_DEPTH;
+  constexpr int R0 = SPW < RING_DEPTH ? SPW : RING_DEPTH;
   constexpr int KSL = SPW * (WTraits<WDT>::bits == 4 ? 128 : 64);
   const int gs = WDT == W_INT4 ? gshift : 5;
   const int sbrow = (KSL >> gs) * (WDT == W_INT4 ? 2 : 1);
