@@ -135,3 +135,46 @@ def test_fp32_accumulation_all_ones(W, M):
     y = W.wq_gemm(dev_bf16(xbits), dev_u8(fp4), W.WQ_E2M1X2, dev_u8(np.full((N, K // 32), 127, np.uint8)),
                   W.WQ_E8M0, 32, N)
     assert np.all(bf16_decode(host_bits16(y)) == 4096.0)
+
+
+@pytest.mark.parametrize("M", [1, 3, 4])
+def test_gemv_int4_zero_rows_and_groups(W, M):
+    # all-zero weight rows must give exactly zero (the bound is zero there);
+    # zeroed groups inside other rows must not disturb the rest
+    K, N = 4096, 200
+    g = np.random.default_rng(500 + M)
+    Wf = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
+    Wf[::7] = 0.0
+    Wf[3, 128:1024] = 0.0
+    Wf[5, :128] = 0.0
+    xbits = to_bf16_bits((g.standard_normal((M, K)) * 3).astype(np.float32))
+    args, wdeq, chan = _prep(W, "int4", Wf)
+    banner("gemv int4 zero rows", M)
+    y = W.wq_gemm(dev_bf16(xbits), *args, N)
+    _check(y, xbits, wdeq, chan)
+    assert np.all(bf16_decode(host_bits16(y))[:, ::7] == 0.0)
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_gemv_int4_offset_activations(W, M):
+    # activations with a large common offset: sum_k x_k dominates every group
+    K, N = 4096, 512
+    g = np.random.default_rng(600 + M)
+    Wf = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
+    xbits = to_bf16_bits((40.0 + g.standard_normal((M, K))).astype(np.float32))
+    args, wdeq, chan = _prep(W, "int4", Wf)
+    banner("gemv int4 offset x", M)
+    _check(W.wq_gemm(dev_bf16(xbits), *args, N), xbits, wdeq, chan)
+
+
+@pytest.mark.parametrize("kind", ["int4", "mxfp4"])
+@pytest.mark.parametrize("M,N", [(1, 300), (4, 272)])
+def test_gemv_long_k(W, kind, M, N):
+    # K = 8192: 16 steps per wave; at M = 4 the workgroup needs more than 64 KB of LDS
+    K = 8192
+    g = np.random.default_rng(700 + M + N)
+    Wf = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
+    xbits = to_bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    args, wdeq, chan = _prep(W, kind, Wf)
+    banner("gemv long K", kind, M, N, K)
+    _check(W.wq_gemm(dev_bf16(xbits), *args, N), xbits, wdeq, chan)

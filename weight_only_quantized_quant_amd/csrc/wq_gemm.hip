@@ -1,14 +1,14 @@
 // Weight-only quantized matmul y[M,N] = x[M,K] . dequant(W[N,K])^T for gfx950.
 //
-// Decode (M <= 16): split-K GEMV.  A workgroup owns 16*TN output columns and
-// S waves; wave w streams the K-slice [w*K/S, (w+1)*K/S) of those rows with
-// 16-byte loads issued up front, converts the packed weights to bf16 in
-// registers and feeds v_mfma_f32_16x16x32_bf16 (x rows beyond M are zero).
-// The S partial 16x16 tiles are reduced through LDS and rounded to bf16 once.
+// Decode (M <= 16): split-K GEMV.  A workgroup owns 16 output columns; its
+// waves split K, stream the packed weights (through a small LDS ring fed by
+// direct-to-LDS loads when M <= 4), convert them to bf16 in registers and feed
+// v_mfma_f32_16x16x32_bf16 with the x rows as the other operand.  The partial
+// 16x16 tiles are reduced through LDS and rounded to bf16 once.
 //
-// Prefill (M > 16): 256x256 output tile per workgroup, 4 waves of 128x128,
-// K step 64 with double-buffered LDS tiles (x in bf16, W still packed); each
-// wave dequantizes its W fragments from LDS in registers right before
+// Prefill (M > 16): 256x256 output tile per workgroup of 8 waves, K step 64,
+// two LDS stages filled by direct-to-LDS loads (x in bf16, W still packed);
+// each wave dequantizes its W fragments from LDS in registers right before
 // v_mfma_f32_32x32x16_bf16.
 #include <hip/hip_runtime.h>
 
@@ -217,151 +217,181 @@ __global__ __launch_bounds__(512) void k_gemv(const uint16_t* __restrict__ x, in
 }
 
 // ---------------------------------------------------------------------------
-// Prefill GEMM
+// Direct-to-LDS loads
 // ---------------------------------------------------------------------------
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int A_STRIDE = BK * 2 + 16;                  // bytes per x row in LDS (padded)
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, (int)voff, 0,
+                                           0, 0);
+}
+// s_waitcnt with vmcnt <= n, other counters unconstrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
 
+// ---------------------------------------------------------------------------
+// Prefill GEMM, 8-wave form
+// ---------------------------------------------------------------------------
+// 256x256 output tile per workgroup of 8 waves (2 along M x 4 along N, each
+// 128x64 with MFMA 32x32x16 bf16), K step 64, two LDS stages.  Two waves share
+// each SIMD, so one wave's MFMAs overlap the other's dequantization and LDS
+// reads.  Tiles arrive by direct-to-LDS buffer loads issued one K step ahead;
+// one barrier per step both publishes the step's tiles and retires the reads
+// of the stage the next loads overwrite.  x rows are 128 bytes in LDS with
+// their 16-byte chunks XOR-swizzled by row (chunk c of row r sits at c ^ (r & 7)),
+// which keeps the 32 lanes reading 32 rows of one chunk on distinct banks.
+// Rows past M or N read as zeros through the buffer range; their results are
+// not stored.
 template <int WDT>
-struct GemmCfg {
-  static constexpr int wbytes = BK * WTraits<WDT>::bits / 8;   // packed bytes per W row per K step
-  static constexpr int B_STRIDE = wbytes + 16;                  // padded
-  static constexpr int A_TILE = BM * A_STRIDE;
-  static constexpr int B_TILE = BN * B_STRIDE;
+struct Gemm8 {
+  static constexpr int BM = 256, BN = 256, BK = 64;
+  static constexpr int wbytes = BK * WTraits<WDT>::bits / 8;   // packed bytes per W row per step
+  static constexpr int A_TILE = BM * BK * 2;                    // 32 KB
+  static constexpr int B_TILE = BN * wbytes;                    // 8 KB (4-bit) or 16 KB (8-bit)
   static constexpr int STAGE = A_TILE + B_TILE;
   static constexpr int LDS = 2 * STAGE;
-  static constexpr int B_CHUNKS = BN * wbytes / 16 / 256;       // 16-byte chunks per thread
+  static constexpr int B_DMA = B_TILE / 1024 / 8;               // 1 KB DMA instructions per wave
 };
 
 template <int WDT>
-__global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ x, int64_t M, int64_t N, int64_t K,
-                                             const uint8_t* __restrict__ w, const void* __restrict__ sc, int group,
-                                             const float* __restrict__ chscale, uint16_t* __restrict__ y,
-                                             int tiles_m, int tiles_n) {
-  using C = GemmCfg<WDT>;
+__global__ __launch_bounds__(512) void k_gemm8(const uint16_t* __restrict__ x, int64_t M, int64_t N, int64_t K,
+                                              const uint8_t* __restrict__ w, const void* __restrict__ sc,
+                                              int group_shift, const float* __restrict__ chscale,
+                                              uint16_t* __restrict__ y, int tiles_m, int tiles_n) {
+  using C = Gemm8<WDT>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int l32 = lane & 31, h = lane >> 5;
 
   // XCD-aware order: consecutive workgroup ids land on different XCDs, so give
-  // each XCD a contiguous range of tiles (m-major, which shares B panels).
+  // each XCD a contiguous range of tiles (m-major, which shares W panels).
   const int nwg = tiles_m * tiles_n;
   int pid = blockIdx.x;
   if (nwg % 8 == 0) pid = (pid % 8) * (nwg / 8) + pid / 8;
   const int tn = pid % tiles_n, tm = pid / tiles_n;
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
   const int64_t rowbytes = K * WTraits<WDT>::bits / 8;
+  const int64_t mrows = M - m0 < C::BM ? M - m0 : C::BM;
+  const int64_t nrows = N - n0 < C::BN ? N - n0 : C::BN;
+  const auto ra = make_rsrc(x + m0 * K, mrows * K * 2);
+  const auto rb = make_rsrc(w + n0 * rowbytes, nrows * rowbytes);
 
-  // global -> LDS copy assignments
-  // x: 256 rows x 128 B: thread covers rows (tid/8) + 32*i, 16-byte chunk tid%8
-  const int a_row = tid >> 3, a_chk = tid & 7;
-  const uint16_t* a_src[8];
+  // DMA assignments.  A: 32 KB per stage = 4 instructions per wave, each 8 rows.
+  uint32_t a_off[4];
 #pragma unroll
-  for (int i = 0; i < 8; i++) {
-    int64_t r = m0 + a_row + 32 * i;
-    r = r < M ? r : M - 1;
-    a_src[i] = x + r * K + a_chk * 8;
+  for (int i = 0; i < 4; i++) {
+    const int r = 8 * (wave * 4 + i) + (lane >> 3);
+    const int c = (lane & 7) ^ (r & 7);
+    a_off[i] = (uint32_t)r * (uint32_t)(K * 2) + 16 * c;
   }
-  // W: BN rows x wbytes: chunks per row = wbytes/16
-  constexpr int CPR = C::wbytes / 16;
-  const uint8_t* b_src[C::B_CHUNKS];
-  int b_dst[C::B_CHUNKS];
+  // B: rows of wbytes, lanes in row order.
+  constexpr int LPR = C::wbytes / 16;                          // lanes per W row
+  uint32_t b_off[C::B_DMA];
 #pragma unroll
-  for (int i = 0; i < C::B_CHUNKS; i++) {
-    const int q = tid + 256 * i;
-    const int r = q / CPR, ch = q % CPR;
-    int64_t n = n0 + r;
-    n = n < N ? n : N - 1;
-    b_src[i] = w + n * rowbytes + ch * 16;
-    b_dst[i] = r * C::B_STRIDE + ch * 16;
+  for (int i = 0; i < C::B_DMA; i++) {
+    const int r = (1024 / C::wbytes) * (wave * C::B_DMA + i) + lane / LPR;
+    b_off[i] = (uint32_t)(r * rowbytes) + 16 * (lane % LPR);
   }
-  // scale rows of this lane's four n-subtiles
-  int64_t srow[4];
-#pragma unroll
-  for (int j = 0; j < 4; j++) {
-    int64_t n = n0 + wn * 128 + 32 * j + l32;
-    srow[j] = n < N ? n : N - 1;
-  }
-
-  f32x16_t acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; i++)
-#pragma unroll
-    for (int j = 0; j < 4; j++)
-#pragma unroll
-      for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
-
-  u32x4_t ra[8], rb[C::B_CHUNKS];
-  float rs[4], cs[4];
-  auto gload = [&](int64_t k0) {
-#pragma unroll
-    for (int i = 0; i < 8; i++) ra[i] = ld16(a_src[i] + k0);
-#pragma unroll
-    for (int i = 0; i < C::B_CHUNKS; i++) rb[i] = ld16(b_src[i] + k0 * WTraits<WDT>::bits / 8);
-#pragma unroll
-    for (int j = 0; j < 4; j++) rs[j] = load_scale<WDT>(sc, srow[j], K, group, k0 + 32 * h);
-  };
-  auto lstore = [&](int stage) {
+  auto issue = [&](int stage, int64_t k0) {
     uint8_t* A = lds + stage * C::STAGE;
     uint8_t* B = A + C::A_TILE;
 #pragma unroll
-    for (int i = 0; i < 8; i++) *reinterpret_cast<u32x4_t*>(A + (a_row + 32 * i) * A_STRIDE + a_chk * 16) = ra[i];
+    for (int i = 0; i < 4; i++) lds_dma16(ra, A + (wave * 4 + i) * 1024, a_off[i] + (uint32_t)(k0 * 2));
 #pragma unroll
-    for (int i = 0; i < C::B_CHUNKS; i++) *reinterpret_cast<u32x4_t*>(B + b_dst[i]) = rb[i];
+    for (int i = 0; i < C::B_DMA; i++)
+      lds_dma16(rb, B + (wave * C::B_DMA + i) * 1024, b_off[i] + (uint32_t)(k0 * WTraits<WDT>::bits / 8));
   };
 
-  const int nk = (int)(K / BK);
-  gload(0);
-  lstore(0);
+  // scale rows of this lane's two 32-column subtiles (clamped; unused past N)
+  int64_t srow[2];
 #pragma unroll
-  for (int j = 0; j < 4; j++) cs[j] = rs[j];
-  __syncthreads();
+  for (int j = 0; j < 2; j++) {
+    const int64_t n = n0 + wn * 64 + 32 * j + l32;
+    srow[j] = n < N ? n : N - 1;
+  }
+  // Scales are prefetched one step ahead as raw bits and converted only after
+  // the next step's wait: converting at the load would make the wave wait for
+  // the tile loads issued just before it.
+  const int gs = WDT == W_INT4 ? group_shift : 5;
+  auto scale_raw = [&](int j, int64_t k0) -> uint32_t {
+    const int64_t kk = (k0 + 32 * h) >> gs;
+    if constexpr (WDT == W_INT4) {
+      return reinterpret_cast<const uint16_t*>(sc)[srow[j] * (K >> gs) + kk];
+    } else if constexpr (WDT == W_FP4) {
+      return reinterpret_cast<const uint8_t*>(sc)[srow[j] * (K >> 5) + kk];
+    } else {
+      return 0u;
+    }
+  };
+  auto scale_val = [](uint32_t raw) -> float {
+    if constexpr (WDT == W_INT4) return __uint_as_float(raw << 16);
+    else if constexpr (WDT == W_FP4) return e8m0_as_scale(raw);
+    else return 1.0f;
+  };
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
+
+  const int nk = (int)(K / C::BK);
+  float cs[2];
+  uint32_t ns[2];
+  issue(0, 0);
+#pragma unroll
+  for (int j = 0; j < 2; j++) ns[j] = scale_raw(j, 0);
 
   for (int kt = 0; kt < nk; kt++) {
     const int stage = kt & 1;
-    if (kt + 1 < nk) gload((int64_t)(kt + 1) * BK);
+    // this wave's loads of step kt are in LDS; the barrier makes every wave's
+    // visible and guarantees stage ^ 1 is no longer being read
+    wait_vm<0>();
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 2; j++) cs[j] = scale_val(ns[j]);
+    if (kt + 1 < nk) {
+      issue(stage ^ 1, (int64_t)(kt + 1) * C::BK);
+#pragma unroll
+      for (int j = 0; j < 2; j++) ns[j] = scale_raw(j, (int64_t)(kt + 1) * C::BK);
+    }
     const uint8_t* A = lds + stage * C::STAGE;
     const uint8_t* B = A + C::A_TILE;
-    // packed W fragments of this lane for the whole K step
-    bf16x8_t bq[4][4];
+    bf16x8_t bq[2][4];
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const uint8_t* bp = B + (wn * 128 + 32 * j + l32) * C::B_STRIDE;
+    for (int j = 0; j < 2; j++) {
+      const uint8_t* bp = B + (wn * 64 + 32 * j + l32) * C::wbytes;
       if constexpr (WTraits<WDT>::bits == 4) {
-        const u32x4_t pw = *reinterpret_cast<const u32x4_t*>(bp + 16 * h);
-        dequant16<WDT>(pw, cs[j], bq[j]);
+        dequant16<WDT>(ld16(bp + 16 * h), cs[j], bq[j]);
       } else {
-        const u32x4_t p0 = *reinterpret_cast<const u32x4_t*>(bp + 32 * h);
-        const u32x4_t p1 = *reinterpret_cast<const u32x4_t*>(bp + 32 * h + 16);
-        dequant16<WDT>(p0, 1.0f, bq[j]);
-        dequant16<WDT>(p1, 1.0f, bq[j] + 2);
+        dequant16<WDT>(ld16(bp + 32 * h), 1.0f, bq[j]);
+        dequant16<WDT>(ld16(bp + 32 * h + 16), 1.0f, bq[j] + 2);
       }
     }
 #pragma unroll
-    for (int s = 0; s < 4; s++) {
+    for (int s4 = 0; s4 < 4; s4++) {
       bf16x8_t af[4];
 #pragma unroll
-      for (int i = 0; i < 4; i++)
-        af[i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(A + (wm * 128 + 32 * i + l32) * A_STRIDE + (32 * h + 8 * s) * 2));
+      for (int i = 0; i < 4; i++) {
+        const int r = wm * 128 + 32 * i + l32;
+        af[i] = as_bf16x8(ld16(A + r * 128 + (((4 * h + s4) ^ (r & 7)) << 4)));
+      }
 #pragma unroll
       for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bq[j][s], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) {
-      __syncthreads();           // everyone is done reading the other stage
-      lstore(stage ^ 1);
-#pragma unroll
-      for (int j = 0; j < 4; j++) cs[j] = rs[j];
-      __syncthreads();
+        for (int j = 0; j < 2; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bq[j][s4], acc[i][j], 0, 0, 0);
     }
   }
 
   // epilogue: C element r of a 32x32 tile sits at row 8*(r/4) + 4*h + r%4, col l32
 #pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const int64_t col = n0 + wn * 128 + 32 * j + l32;
+  for (int j = 0; j < 2; j++) {
+    const int64_t col = n0 + wn * 64 + 32 * j + l32;
     if (col >= N) continue;
     float cscale = 1.0f;
     if constexpr (WDT == W_FP8) cscale = chscale[col];
@@ -389,15 +419,20 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ x, in
 // the slice are fetched the same way once.  MFMA rows >= M read row 0 of x;
 // those output rows are discarded.
 
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, (int)voff, 0,
-                                           0, 0);
-}
-// s_waitcnt with vmcnt <= n, other counters unconstrained (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+// Kernels that may take more than 64 KB of dynamic LDS raise their limit to the
+// CU's 160 KB once per device before their first launch there.
+template <auto KERNEL>
+hipError_t allow_lds(size_t bytes) {
+  static bool done[64] = {};
+  if (bytes <= 65536) return hipSuccess;
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64 && done[dev]) return hipSuccess;
+  const hipError_t f =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(KERNEL), hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (f == hipSuccess && dev >= 0 && dev < 64) done[dev] = true;
+  return f;
 }
 
 template <int WDT, int SPW, int R, int NW>
@@ -564,7 +599,7 @@ void gemv_nstep(const GemvSplit& sp, const uint16_t* x, int64_t M, int64_t N, in
 constexpr int RING_NW = 4;
 constexpr int RING_DEPTH = 2;
 template <int WDT, int SPW>
-void ring_go(int64_t M, const uint16_t* x, int64_t N, int64_t K, const uint8_t* w, const void* sc, int gshift,
+wq_status ring_go(int64_t M, const uint16_t* x, int64_t N, int64_t K, const uint8_t* w, const void* sc, int gshift,
              const float* ch, uint16_t* y, hipStream_t s) {
   constexpr int R0 = SPW < RING_DEPTH ? SPW : RING_DEPTH;
   constexpr int KSL = SPW * (WTraits<WDT>::bits == 4 ? 128 : 64);
@@ -577,10 +612,13 @@ void ring_go(int64_t M, const uint16_t* x, int64_t N, int64_t K, const uint8_t* 
   const size_t budget = (size_t)160 * 1024 * RING_NW / 16;
   if (R0 >= 7 && lds_for(R0) > budget && lds_for(R0 - 1) <= budget) {
     constexpr int R = R0 >= 7 ? R0 - 1 : R0;
+    if (allow_lds<k_gemv_ring<WDT, SPW, R, RING_NW>>(lds_for(R)) != hipSuccess) return WQ_EHIP;
     k_gemv_ring<WDT, SPW, R, RING_NW><<<grid, 64 * RING_NW, lds_for(R), s>>>(x, (int)M, N, K, w, sc, gshift, ch, y);
   } else {
+    if (allow_lds<k_gemv_ring<WDT, SPW, R0, RING_NW>>(lds_for(R0)) != hipSuccess) return WQ_EHIP;
     k_gemv_ring<WDT, SPW, R0, RING_NW><<<grid, 64 * RING_NW, lds_for(R0), s>>>(x, (int)M, N, K, w, sc, gshift, ch, y);
   }
+  return WQ_OK;
 }
 
 template <int WDT>
@@ -591,14 +629,15 @@ wq_status launch_gemv(const uint16_t* x, int64_t M, int64_t N, int64_t K, const 
   if (M <= 4 && K % (KSTEP * RING_NW) == 0 && 16 * K * 2 <= 0x7FFFFFF0LL) {
     const int64_t spw = K / (KSTEP * RING_NW);
     if (spw == 1 || spw == 2 || spw == 4 || spw == 8 || spw == 16) {
+      wq_status st;
       switch (spw) {
-        case 1: ring_go<WDT, 1>(M, x, N, K, w, sc, gshift, ch, y, s); break;
-        case 2: ring_go<WDT, 2>(M, x, N, K, w, sc, gshift, ch, y, s); break;
-        case 4: ring_go<WDT, 4>(M, x, N, K, w, sc, gshift, ch, y, s); break;
-        case 8: ring_go<WDT, 8>(M, x, N, K, w, sc, gshift, ch, y, s); break;
-        default: ring_go<WDT, 16>(M, x, N, K, w, sc, gshift, ch, y, s); break;
+        case 1: st = ring_go<WDT, 1>(M, x, N, K, w, sc, gshift, ch, y, s); break;
+        case 2: st = ring_go<WDT, 2>(M, x, N, K, w, sc, gshift, ch, y, s); break;
+        case 4: st = ring_go<WDT, 4>(M, x, N, K, w, sc, gshift, ch, y, s); break;
+        case 8: st = ring_go<WDT, 8>(M, x, N, K, w, sc, gshift, ch, y, s); break;
+        default: st = ring_go<WDT, 16>(M, x, N, K, w, sc, gshift, ch, y, s); break;
       }
-      return wq_launch_status();
+      return st != WQ_OK ? st : wq_launch_status();
     }
   }
   constexpr int MAXSTEP = WTraits<WDT>::bits == 4 ? 4 : 8;
@@ -619,16 +658,13 @@ wq_status launch_gemv(const uint16_t* x, int64_t M, int64_t N, int64_t K, const 
 template <int WDT>
 wq_status launch_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w, const void* sc, int group,
                       const float* ch, uint16_t* y, hipStream_t s) {
-  using C = GemmCfg<WDT>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)k_gemm<WDT>, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS) !=
-        hipSuccess)
-      return WQ_EHIP;
-    attr_set = true;
-  }
-  const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
-  k_gemm<WDT><<<(unsigned)(tm * tn), 256, C::LDS, s>>>(x, M, N, K, w, sc, group, ch, y, tm, tn);
+  using C8 = Gemm8<WDT>;
+  // 32-bit buffer offsets: one 256-row x tile and one 256-row W tile
+  if ((int64_t)C8::BM * K * 2 > 0x7FFFFFF0LL) return WQ_EINVAL;
+  if (allow_lds<k_gemm8<WDT>>(C8::LDS) != hipSuccess) return WQ_EHIP;
+  const int tm = (int)((M + C8::BM - 1) / C8::BM), tn = (int)((N + C8::BN - 1) / C8::BN);
+  const int gshift = group == 32 ? 5 : group == 64 ? 6 : 7;
+  k_gemm8<WDT><<<(unsigned)(tm * tn), 512, C8::LDS, s>>>(x, M, N, K, w, sc, gshift, ch, y, tm, tn);
   return wq_launch_status();
 }
 
@@ -652,7 +688,7 @@ wq_status wq_gemm(const void* x_bf16, int64_t M, int64_t N, int64_t K, const voi
   else if (w_dtype == WQ_E2M1X2 && s_dtype == WQ_E8M0 && group == 32) wdt = W_FP4;
   else if (w_dtype == WQ_E4M3 && s_dtype == WQ_F32 && group == K) wdt = W_FP8;
   else return WQ_EUNSUPPORTED;
-  if (M > 16 && (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN) > 0x7FFFFFFF) return WQ_EINVAL;
+  if (M > 16 && (int64_t)((M + 255) / 256) * ((N + 255) / 256) > 0x7FFFFFFF) return WQ_EINVAL;   // prefill tiles
   hipStream_t s = (hipStream_t)stream;
   const uint16_t* x = (const uint16_t*)x_bf16;
   const uint8_t* w = (const uint8_t*)wqp;
