@@ -169,6 +169,86 @@ wq_status wq_gemm(const void* x_bf16, int64_t M, int64_t N, int64_t K,
 /* Bytes of workspace wq_gemm needs for this problem (currently always 0). */
 size_t wq_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int w_dtype, int32_t group);
 
+/*
+ * W4A8 mixture-of-experts path
+ * ----------------------------
+ * Defined by "Production-Ready W4A8: vLLM Integration and Quality Recovery
+ * Techniques Explained" (Cohere), sections "High-Performance W4A8 GEMM Kernel"
+ * (INT4 weights become FP8 through a table of the 16 products s * w of a group's
+ * fp8 scale s, built from the scale inside the main loop, then an fp8 x fp8
+ * multiply with fp32 accumulation) and "Accurate W4A8 Kernel" (group scales
+ * quantized to fp8 with an fp32 channel scale, 1/8 on the fp8 scales and 8 on
+ * the channel scale so that every s * w stays in range; per-token and
+ * per-channel fp32 scales applied at the end).  INT4 groups are 128 elements
+ * along K.
+ */
+
+/*
+ * wq_moe_route -- softmax over the E expert logits of each token, the k most
+ * probable experts, and the grouping of the T*k (token, expert) pairs.
+ *
+ * logits     T x E fp32.  1 <= k <= E <= 64; T*k < 2^31.
+ * ids        T x k int32 (output): experts in decreasing logit order (equal
+ *            logits: lower expert id first).
+ * weights    T x k fp32 (output): their softmax probabilities (fp32 arithmetic;
+ *            not re-normalised).
+ * offsets    E + 1 int32 (output): grouped rows of expert e are
+ *            [offsets[e], offsets[e + 1]); offsets[E] = T*k.
+ * row_token  T*k int32 (output): token of each grouped row, increasing within
+ *            an expert.
+ * row_slot   T*k int32 (output): position of the expert in that token's ids.
+ * Non-finite logits are outside the contract.
+ */
+wq_status wq_moe_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* ids, float* weights,
+                       int32_t* offsets, int32_t* row_token, int32_t* row_slot, void* stream);
+
+/*
+ * wq_w4a8_prepack -- one-time preparation of INT4 expert weights for
+ * wq_moe_gemm_w4a8.
+ *
+ * wq       experts x N x K/8 uint32 INT4X8 words (group 128 along K).
+ * scales   experts x N x K/128 bf16 group scales.
+ * wq_out   experts x N x K/8 uint32 (output, may alias wq): the same codes with
+ *          the nibbles of every word interleaved (element j < 4 of a word in
+ *          nibble 2j, element j >= 4 in nibble 2(j-4)+1), the layout the GEMM's
+ *          table lookups read.
+ * s8       experts x N x K/128 E4M3 codes (output): e4m3(RN_f32(s / ch)).
+ * ch       experts x N fp32 (output): 8 * RN_f32(max_g |s| / 448), with
+ *          RN_f32(...) replaced by 1 for an all-zero channel.
+ * K % 128 == 0.  Non-finite scales are outside the contract.
+ */
+wq_status wq_w4a8_prepack(const uint32_t* wq, const uint16_t* scales, int64_t experts, int64_t N, int64_t K,
+                          uint32_t* wq_out, uint8_t* s8, float* ch, void* stream);
+
+/*
+ * wq_w4a8_dequant -- the E4M3 weights the grouped GEMM multiplies, written
+ * out: codes[n, k] = e4m3(w[n, k] * val(s8[n, k / 128])), rounded to nearest
+ * even, saturating at 448 (the table lookup of wq_moe_gemm_w4a8, same device
+ * code).  wq: N x K/8 words in the wq_w4a8_prepack layout; s8: N x K/128;
+ * codes: N x K bytes (output).
+ */
+wq_status wq_w4a8_dequant(const uint32_t* wq, const uint8_t* s8, int64_t N, int64_t K, uint8_t* codes, void* stream);
+
+/*
+ * wq_moe_gemm_w4a8 -- grouped GEMM over experts:
+ *   y[r, n] = bf16( a_scale[t] * ch[e, n] * sum_k val(x8[t, k]) * val(W8[e, n, k]) )
+ * for grouped row r of expert e (offsets[e] <= r < offsets[e + 1]), token
+ * t = row_token[r] (t = r when row_token is NULL, which requires R == T), and
+ * W8 the table-looked-up E4M3 weights (see wq_w4a8_dequant), fp32 accumulation.
+ *
+ * x8        T x K E4M3 codes (per-token quantized activations), a_scale T fp32
+ *           (quantize_e4m3 with block -1 produces both).  T*K < 2^31.
+ * row_token R int32 or NULL; offsets experts + 1 int32 (device), offsets[0] = 0,
+ *           non-decreasing, offsets[experts] = R.
+ * wq, s8, ch  from wq_w4a8_prepack, experts x N x ...; K % 128 == 0.
+ * y         R x N bf16 (output), rows in grouped order.
+ * The fp8 MFMA treats E4M3 subnormal operands as zero; results differ from the
+ * exact product by at most the flushed terms.
+ */
+wq_status wq_moe_gemm_w4a8(const uint8_t* x8, int64_t T, const float* a_scale, const int32_t* row_token, int64_t R,
+                           const int32_t* offsets, int32_t experts, int64_t N, int64_t K, const uint32_t* wq,
+                           const uint8_t* s8, const float* ch, uint16_t* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

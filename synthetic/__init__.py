@@ -113,3 +113,23 @@ def moe_expert_weight(expert: int, which: str, seed: int = 2, hidden: int = 4096
 
 def moe_down_input(seed: int = 3, rows: int = 32768, inter: int = 1536) -> np.ndarray:
     return to_bf16_bits(rng(seed).standard_normal((rows, inter), dtype=np.float32))
+
+
+def moe_expert_weight_gpu(expert: int, which: str, seed: int = 2, hidden: int = 4096, inter: int = 1536,
+                          device: str = "cuda"):
+    """Device-side stand-in for moe_expert_weight (torch's Philox generator, one
+    stream per (seed, expert, which)); same shapes and N(0, 0.02) distribution.
+    Used where host generation of all experts would take minutes."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 1_000_003 + int(expert) * 2 + (0 if which == "gate_up" else 1))
+    shape = (2 * inter, hidden) if which == "gate_up" else (hidden, inter)
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32) * 0.02
+
+
+def moe_down_input_gpu(seed: int = 3, rows: int = 32768, inter: int = 1536, device: str = "cuda"):
+    """Device-side stand-in for moe_down_input: bf16 N(0, 1) rows in grouped order."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 1_000_003 + 7)
+    return torch.randn((rows, inter), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)

@@ -27,7 +27,8 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("quantize_e4m3", "quantize_mxfp4", "quantize_int4", "wq_dequant", "wq_gemm",
-              "wq_gemm_workspace_size", "wq_status_string"):
+              "wq_gemm_workspace_size", "wq_status_string", "wq_moe_route", "wq_w4a8_prepack",
+              "wq_w4a8_dequant", "wq_moe_gemm_w4a8"):
         assert n in names
 
 
@@ -92,3 +93,32 @@ def test_invalid_arguments_rejected_before_launch(lib):
     assert gm(*args(1, 16, 128, 5, 1, 128, x=q)) == 2
     lib.wq_gemm_workspace_size.restype = ctypes.c_size_t
     assert lib.wq_gemm_workspace_size(_i64(1), _i64(16), _i64(128), 5, 128) == 0
+
+
+
+def test_moe_invalid_arguments_rejected_before_launch(lib):
+    p = ctypes.c_void_p(0x1000)
+    q = ctypes.c_void_p(0x1004)          # misaligned
+    r = lib.wq_moe_route
+    r.restype = ctypes.c_int
+    assert r(p, _i64(16), 65, 8, p, p, p, p, p, None) == 1               # more than 64 experts
+    assert r(p, _i64(16), 8, 9, p, p, p, p, p, None) == 1                # k > E
+    assert r(p, _i64(16), 8, 0, p, p, p, p, p, None) == 1
+    assert r(p, _i64(-1), 8, 2, p, p, p, p, p, None) == 1
+    assert r(p, _i64(16), 8, 2, p, p, None, p, p, None) == 1             # offsets NULL
+    pk = lib.wq_w4a8_prepack
+    pk.restype = ctypes.c_int
+    assert pk(p, p, _i64(2), _i64(16), _i64(100), p, p, p, None) == 1   # K % 128
+    assert pk(p, p, _i64(0), _i64(16), _i64(128), p, p, p, None) == 1
+    assert pk(q, p, _i64(2), _i64(16), _i64(128), p, p, p, None) == 2
+    assert pk(p, None, _i64(2), _i64(16), _i64(128), p, p, p, None) == 1
+    dq = lib.wq_w4a8_dequant
+    dq.restype = ctypes.c_int
+    assert dq(p, p, _i64(4), _i64(64), p, None) == 1
+    gm = lib.wq_moe_gemm_w4a8
+    gm.restype = ctypes.c_int
+    args = lambda T, R, K, rt=p, x=p: (x, _i64(T), p, rt, _i64(R), p, 4, _i64(64), _i64(K), p, p, p, p, None)
+    assert gm(*args(16, 32, 100)) == 1                                   # K % 128
+    assert gm(*args(16, 32, 128, rt=None)) == 1                          # identity rows need R == T
+    assert gm(*args(16, 32, 128, x=q)) == 2
+    assert gm(*args(0, 0, 128)) == 1

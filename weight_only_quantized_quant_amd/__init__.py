@@ -39,6 +39,10 @@ _SIGS = {
     "wq_gemm": ([_vp, _i64, _i64, _i64, _vp, ctypes.c_int, _vp, ctypes.c_int, _i32, _vp, _vp, _sz, _vp],
                 ctypes.c_int),
     "wq_gemm_workspace_size": ([_i64, _i64, _i64, ctypes.c_int, _i32], _sz),
+    "wq_moe_route": ([_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "wq_w4a8_prepack": ([_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "wq_w4a8_dequant": ([_vp, _vp, _i64, _i64, _vp, _vp], ctypes.c_int),
+    "wq_moe_gemm_w4a8": ([_vp, _i64, _vp, _vp, _i64, _vp, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -189,4 +193,90 @@ def wq_gemm(x: torch.Tensor, wq: torch.Tensor, w_dtype: int, w_scales: torch.Ten
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     _check(lib.wq_gemm(x.data_ptr(), M, N, K, wq.data_ptr(), w_dtype, sp, s_dtype, group, y.data_ptr(), ws_ptr,
                        ws_bytes, _stream()), "wq_gemm")
+    return y
+
+
+# ---------------------------------------------------------------------------
+# W4A8 mixture of experts
+# ---------------------------------------------------------------------------
+def _typed(t, dtype, shape, name):
+    _dev(t, name)
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {dtype} of shape {tuple(shape)}")
+
+
+def wq_moe_route(logits: torch.Tensor, k: int):
+    """logits fp32 [T, E] -> (ids int32 [T, k], weights fp32 [T, k], offsets int32 [E + 1],
+    row_token int32 [T*k], row_slot int32 [T*k])."""
+    _dev(logits, "logits")
+    if logits.dtype != torch.float32 or logits.dim() != 2:
+        raise ValueError("logits must be a 2-D float32 tensor")
+    T, E = logits.shape
+    d = logits.device
+    ids = torch.empty((T, k), dtype=torch.int32, device=d)
+    weights = torch.empty((T, k), dtype=torch.float32, device=d)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=d)
+    row_token = torch.empty(T * k, dtype=torch.int32, device=d)
+    row_slot = torch.empty(T * k, dtype=torch.int32, device=d)
+    _check(lib.wq_moe_route(logits.data_ptr(), T, E, k, ids.data_ptr(), weights.data_ptr(), offsets.data_ptr(),
+                            row_token.data_ptr(), row_slot.data_ptr(), _stream()), "wq_moe_route")
+    return ids, weights, offsets, row_token, row_slot
+
+
+def wq_w4a8_prepack(wq: torch.Tensor, scales: torch.Tensor, wq_out=None):
+    """wq int32 [E, N, K/8] INT4X8 words, scales bf16 [E, N, K/128] ->
+    (re-laid words int32 [E, N, K/8], s8 uint8 [E, N, K/128], ch fp32 [E, N])."""
+    _dev(wq, "wq")
+    if wq.dtype != torch.int32 or wq.dim() != 3:
+        raise ValueError("wq must be int32 [experts, N, K/8]")
+    E, N, K8 = wq.shape
+    K = 8 * K8
+    _typed(scales, torch.bfloat16, (E, N, K // 128), "scales")
+    wq_out = _out(wq_out, (E, N, K8), torch.int32, wq.device, "wq_out")
+    s8 = torch.empty((E, N, K // 128), dtype=torch.uint8, device=wq.device)
+    ch = torch.empty((E, N), dtype=torch.float32, device=wq.device)
+    _check(lib.wq_w4a8_prepack(wq.data_ptr(), scales.data_ptr(), E, N, K, wq_out.data_ptr(), s8.data_ptr(),
+                               ch.data_ptr(), _stream()), "wq_w4a8_prepack")
+    return wq_out, s8, ch
+
+
+def wq_w4a8_dequant(wq: torch.Tensor, s8: torch.Tensor):
+    """Re-laid words int32 [N, K/8] + s8 [N, K/128] -> E4M3 codes uint8 [N, K]."""
+    _dev(wq, "wq")
+    N, K8 = wq.shape
+    K = 8 * K8
+    _typed(s8, torch.uint8, (N, K // 128), "s8")
+    codes = torch.empty((N, K), dtype=torch.uint8, device=wq.device)
+    _check(lib.wq_w4a8_dequant(wq.data_ptr(), s8.data_ptr(), N, K, codes.data_ptr(), _stream()), "wq_w4a8_dequant")
+    return codes
+
+
+def wq_moe_gemm_w4a8(x8: torch.Tensor, a_scale: torch.Tensor, row_token, offsets: torch.Tensor,
+                     wq: torch.Tensor, s8: torch.Tensor, ch: torch.Tensor, y=None):
+    """Grouped W4A8 GEMM.  x8 uint8 [T, K], a_scale fp32 [T], row_token int32 [R] or None
+    (R = T), offsets int32 [E + 1], wq int32 [E, N, K/8] (re-laid), s8 uint8 [E, N, K/128],
+    ch fp32 [E, N] -> y bf16 [R, N] in grouped row order."""
+    _dev(x8, "x8")
+    if x8.dtype != torch.uint8 or x8.dim() != 2:
+        raise ValueError("x8 must be uint8 [T, K]")
+    T, K = x8.shape
+    _typed(a_scale, torch.float32, (T,), "a_scale")
+    E, N, K8 = wq.shape
+    if 8 * K8 != K:
+        raise ValueError("wq and x8 disagree on K")
+    _typed(wq, torch.int32, (E, N, K8), "wq")
+    _typed(s8, torch.uint8, (E, N, K // 128), "s8")
+    _typed(ch, torch.float32, (E, N), "ch")
+    _typed(offsets, torch.int32, (E + 1,), "offsets")
+    if row_token is None:
+        R, rt = T, None
+    else:
+        _dev(row_token, "row_token")
+        if row_token.dtype != torch.int32 or row_token.dim() != 1:
+            raise ValueError("row_token must be int32 [R]")
+        R, rt = row_token.shape[0], row_token.data_ptr()
+    y = _out(y, (R, N), torch.bfloat16, x8.device, "y")
+    _check(lib.wq_moe_gemm_w4a8(x8.data_ptr(), T, a_scale.data_ptr(), rt, R, offsets.data_ptr(), E, N, K,
+                                wq.data_ptr(), s8.data_ptr(), ch.data_ptr(), y.data_ptr(), _stream()),
+           "wq_moe_gemm_w4a8")
     return y

@@ -27,7 +27,6 @@ template <> struct WTraits<W_INT4> { static constexpr int bits = 4; };
 template <> struct WTraits<W_FP4> { static constexpr int bits = 4; };
 template <> struct WTraits<W_FP8> { static constexpr int bits = 8; };
 
-__device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   return __builtin_bit_cast(bf16x8_t, u32x4_t{a, b, c, d});
 }
@@ -75,16 +74,6 @@ __device__ __forceinline__ void dequant16(u32x4_t w, float s, bf16x8_t out[4]) {
 // ---------------------------------------------------------------------------
 // Decode GEMV
 // ---------------------------------------------------------------------------
-// Raw buffer resources: loads past `bytes` return zeros, which pads the rows
-// beyond N and the x rows beyond M without branches.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int64_t lim = bytes < 0 ? 0 : (bytes > 0x7FFFFFF0LL ? 0x7FFFFFF0LL : bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)lim, 0x00020000);
-}
-__device__ __forceinline__ u32x4_t bld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
-}
-
 template <int WDT>
 __device__ __forceinline__ float scale_of(__amdgpu_buffer_rsrc_t r, uint32_t idx) {
   if constexpr (WDT == W_INT4) return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, (int)(idx * 2), 0, 0));
@@ -214,20 +203,6 @@ __global__ __launch_bounds__(512) void k_gemv(const uint16_t* __restrict__ x, in
     if constexpr (WDT == W_FP8) s *= chscale[col];
     y[(int64_t)m * N + col] = (uint16_t)f32_to_bf16_bits(s);
   }
-}
-
-// ---------------------------------------------------------------------------
-// Direct-to-LDS loads
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, (int)voff, 0,
-                                           0, 0);
-}
-// s_waitcnt with vmcnt <= n, other counters unconstrained (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 // ---------------------------------------------------------------------------

@@ -1,0 +1,448 @@
+// W4A8 mixture-of-experts path for gfx950: routing, grouping of the
+// (token, expert) pairs by expert, the fp8 recipe for the INT4 group scales,
+// and the grouped GEMM whose INT4 weights become E4M3 through a per-group
+// byte table and meet E4M3 activations on fp8 MFMA.
+//
+// Routing: one wave per token with lane e holding expert e's logit; softmax by
+// butterfly reductions (every lane ends with the same sum); top-k by k rounds
+// of a wave argmax in which equal logits resolve towards the lower expert id.
+// Grouping: one workgroup per expert counts the pairs that chose a lower
+// expert (its first row) and walks the tokens in order, placing the tokens
+// that chose it with a block-wide prefix sum: rows of an expert are in
+// increasing token order, and no atomics are involved.
+//
+// Tables: for an fp8 group scale v there are 16 products w * v over the INT4
+// codes w.  A lane keeps them as two 8-byte pools (codes for w = 0..7, and for
+// w = -8..-1, the latter being the positive magnitudes with the sign bit
+// flipped, exact since rounding to nearest even is sign-symmetric) and looks a
+// nibble up with v_perm_b32 in each pool and one more v_perm_b32 keyed on the
+// nibble's sign bit.  The weights are re-laid once so that the even nibble
+// slots of a word hold its elements 0..3 and the odd slots 4..7: one shift and
+// one mask then give four table indices in k order.
+//
+// Grouped GEMM: 256 x 256 tiles of (rows of one expert) x (output channels),
+// 8 waves of 128 x 64, K step 128 = one INT4 group, two LDS stages filled by
+// direct-to-LDS loads; the activation rows are gathered through row_token.
+// v_mfma_scale_f32_32x32x64_f8f6f4 with neutral block scales multiplies the
+// E4M3 operands; the epilogue applies the per-token and per-channel fp32
+// scales and rounds to bf16 once.  The fp8 MFMA treats E4M3 subnormal
+// operands as zero.
+#include <hip/hip_runtime.h>
+
+#include "wq.h"
+#include "wq_device.h"
+#include "wq_host.h"
+
+using namespace wq;
+
+namespace {
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------------------
+// Routing and grouping
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, int64_t T, int E, int k,
+                                               int32_t* __restrict__ ids, float* __restrict__ wts) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;                                   // whole wave
+  const bool valid = lane < E;
+  const float z = valid ? logits[t * E + lane] : 0.0f;
+  float m = valid ? z : -INFINITY;
+  for (int o = 1; o < 64; o <<= 1) m = __builtin_fmaxf(m, __shfl_xor(m, o, 64));
+  const float p = valid ? expf(z - m) : 0.0f;
+  float sum = p;
+  for (int o = 1; o < 64; o <<= 1) sum += __shfl_xor(sum, o, 64);
+  bool avail = valid;
+  for (int j = 0; j < k; j++) {
+    float bv = z;
+    int bi = lane;
+    int bo = avail ? 1 : 0;
+    for (int o = 1; o < 64; o <<= 1) {
+      const float v2 = __shfl_xor(bv, o, 64);
+      const int i2 = __shfl_xor(bi, o, 64);
+      const int o2 = __shfl_xor(bo, o, 64);
+      const bool better = o2 && (!bo || v2 > bv || (v2 == bv && i2 < bi));
+      if (better) {
+        bv = v2;
+        bi = i2;
+        bo = o2;
+      }
+    }
+    const float pw = __shfl(p, bi, 64);
+    if (lane == 0) {
+      ids[t * k + j] = bi;
+      wts[t * k + j] = pw / sum;
+    }
+    if (lane == bi) avail = false;
+  }
+}
+
+__global__ __launch_bounds__(1024) void k_group(const int32_t* __restrict__ ids, int64_t T, int E, int k,
+                                                int32_t* __restrict__ offsets, int32_t* __restrict__ row_token,
+                                                int32_t* __restrict__ row_slot) {
+  __shared__ int red[16];
+  const int e = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t P = T * k;
+  int below = 0;
+  for (int64_t i = tid; i < P; i += 1024) below += ids[i] < e ? 1 : 0;
+  for (int o = 1; o < 64; o <<= 1) below += __shfl_xor(below, o, 64);
+  if (lane == 0) red[wv] = below;
+  __syncthreads();
+  int first = 0;
+  for (int w = 0; w < 16; w++) first += red[w];
+  __syncthreads();
+  int base = first;
+  for (int64_t t0 = 0; t0 < T; t0 += 1024) {
+    const int64_t t = t0 + tid;
+    int slot = -1;
+    if (t < T)
+      for (int j = 0; j < k; j++)
+        if (ids[t * k + j] == e) slot = j;
+    const unsigned long long b = __ballot(slot >= 0);
+    const int pre = __popcll(b & ((1ull << lane) - 1ull));
+    if (lane == 0) red[wv] = __popcll(b);
+    __syncthreads();
+    int wb = 0, tot = 0;
+    for (int w = 0; w < 16; w++) {
+      const int c = red[w];
+      wb += w < wv ? c : 0;
+      tot += c;
+    }
+    if (slot >= 0) {
+      row_token[base + wb + pre] = (int32_t)t;
+      row_slot[base + wb + pre] = slot;
+    }
+    base += tot;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    offsets[e] = first;
+    if (e == E - 1) offsets[E] = (int32_t)P;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Scale recipe, weight re-layout, tables
+// ---------------------------------------------------------------------------
+// One wave per output channel: ch = 8 * RN(amax / 448) (1 for an all-zero
+// channel), s8 = e4m3(RN(s / ch)) with correctly rounded division.
+__global__ __launch_bounds__(256) void k_w4a8_scales(const uint16_t* __restrict__ sc, int64_t rows, int G,
+                                                     uint8_t* __restrict__ s8, float* __restrict__ ch) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  float amax = 0.0f;
+  for (int g = lane; g < G; g += 64) amax = __builtin_fmaxf(amax, __builtin_fabsf(bf16_to_f32(sc[r * G + g])));
+  for (int o = 1; o < 64; o <<= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, o, 64));
+  float s = amax / 448.0f;
+  if (s == 0.0f) s = 1.0f;
+  const float c = 8.0f * s;
+  for (int g = lane; g < G; g += 64) {
+    const float v = bf16_to_f32(sc[r * G + g]) / c;
+    s8[r * G + g] = (uint8_t)(e4m3_pack2<false>(clamp448(v), 0.0f, 0u) & 0xFFu);
+  }
+  if (lane == 0) ch[r] = c;
+}
+
+// Element 8i + j of a word moves from nibble j to nibble 2j (j < 4) or
+// 2(j - 4) + 1 (j >= 4).
+__device__ __forceinline__ uint32_t interleave_nibbles(uint32_t w) {
+  uint32_t o = 0;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    o |= ((w >> (4 * j)) & 0xFu) << (8 * j);
+    o |= ((w >> (4 * j + 16)) & 0xFu) << (8 * j + 4);
+  }
+  return o;
+}
+
+__global__ __launch_bounds__(256) void k_w4a8_relayout(const uint32_t* __restrict__ in, uint32_t* out, int64_t words) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= words) return;                               // words % 4 == 0
+  const u32x4_t v = *reinterpret_cast<const u32x4_t*>(in + i);
+  *reinterpret_cast<u32x4_t*>(out + i) =
+      u32x4_t{interleave_nibbles(v[0]), interleave_nibbles(v[1]), interleave_nibbles(v[2]), interleave_nibbles(v[3])};
+}
+
+// Byte pools of one group: lo = codes of w = 0..7, hi = codes of w = -8..-1.
+struct Lut {
+  uint32_t lo0, lo1, hi0, hi1;
+};
+__device__ __forceinline__ Lut make_lut(uint32_t s8code) {
+  const float v = __builtin_amdgcn_cvt_f32_fp8((int)s8code, 0);
+  uint32_t a = e4m3_pack2<false>(clamp448(v), clamp448(2.0f * v), 0u);          // P1 P2
+  a = e4m3_pack2<true>(clamp448(3.0f * v), clamp448(4.0f * v), a);              // P3 P4
+  uint32_t b = e4m3_pack2<false>(clamp448(5.0f * v), clamp448(6.0f * v), 0u);   // P5 P6
+  b = e4m3_pack2<true>(clamp448(7.0f * v), clamp448(8.0f * v), b);              // P7 P8
+  Lut L;
+  L.lo0 = (a << 8) | (s8code & 0x80u);                                        // +-0 P1 P2 P3
+  L.lo1 = __builtin_amdgcn_perm(b, a, 0x06050403u);                             // P4 P5 P6 P7
+  L.hi0 = __builtin_amdgcn_perm(b, a, 0x04050607u) ^ 0x80808080u;               // -P8 -P7 -P6 -P5
+  L.hi1 = __builtin_amdgcn_perm(b, a, 0x00010203u) ^ 0x80808080u;               // -P4 -P3 -P2 -P1
+  return L;
+}
+// One re-laid word (8 INT4 codes) -> 8 E4M3 codes in k order.
+__device__ __forceinline__ void lut_word(uint32_t w, const Lut& L, uint32_t& d0, uint32_t& d1) {
+  const uint32_t se = w & 0x07070707u, so = (w >> 4) & 0x07070707u;
+  const uint32_t le = __builtin_amdgcn_perm(L.lo1, L.lo0, se), he = __builtin_amdgcn_perm(L.hi1, L.hi0, se);
+  const uint32_t lo = __builtin_amdgcn_perm(L.lo1, L.lo0, so), ho = __builtin_amdgcn_perm(L.hi1, L.hi0, so);
+  const uint32_t me = ((w >> 1) & 0x04040404u) | 0x03020100u;                  // byte k from he if sign bit
+  const uint32_t mo = ((w >> 5) & 0x04040404u) | 0x03020100u;
+  d0 = __builtin_amdgcn_perm(he, le, me);
+  d1 = __builtin_amdgcn_perm(ho, lo, mo);
+}
+
+// Materialised E4M3 weights (N x K codes) from re-laid words and s8.
+__global__ __launch_bounds__(256) void k_w4a8_dequant(const uint32_t* __restrict__ wq, const uint8_t* __restrict__ s8,
+                                                      int64_t N, int64_t K, uint8_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // word index
+  const int64_t wpr = K / 8;
+  if (i >= N * wpr) return;
+  const int64_t n = i / wpr, k = (i % wpr) * 8;
+  const Lut L = make_lut(s8[n * (K / 128) + k / 128]);
+  uint32_t d0, d1;
+  lut_word(wq[i], L, d0, d1);
+  *reinterpret_cast<uint2*>(out + n * K + k) = uint2{d0, d1};
+}
+
+// ---------------------------------------------------------------------------
+// Grouped GEMM
+// ---------------------------------------------------------------------------
+constexpr int MBM = 256, MBN = 256, MBK = 128;
+constexpr int MA_TILE = MBM * MBK;                      // 32 KB of E4M3 rows
+constexpr int MB_TILE = MBN * MBK / 2;                  // 16 KB of packed INT4
+constexpr int MSTAGE = MA_TILE + MB_TILE;
+constexpr int MLDS = 2 * MSTAGE;                        // 96 KB
+
+__global__ __launch_bounds__(512) void k_moe_gemm(const uint8_t* __restrict__ x8, int64_t T,
+                                                  const float* __restrict__ a_scale,
+                                                  const int32_t* __restrict__ row_token,
+                                                  const int32_t* __restrict__ offsets, int E, int64_t N, int64_t K,
+                                                  const uint32_t* __restrict__ wq, const uint8_t* __restrict__ s8,
+                                                  const float* __restrict__ ch, uint16_t* __restrict__ y,
+                                                  int tiles_n) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ int tinfo[2];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int l32 = lane & 31, h = lane >> 5;
+
+  const int nwg = (int)gridDim.x;
+  int pid = blockIdx.x;
+  if (nwg % 8 == 0) pid = (pid % 8) * (nwg / 8) + pid / 8;
+  const int tn = pid % tiles_n, mt = pid / tiles_n;
+
+  // which expert and which of its 256-row tiles this workgroup owns
+  if (wave == 0) {
+    if (lane == 0) tinfo[0] = -1;
+    int before = 0;
+    for (int e0 = 0; e0 < E; e0 += 64) {
+      const int e = e0 + lane;
+      const int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
+      const int tiles = (cnt + MBM - 1) / MBM;
+      int incl = tiles;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += v;
+      }
+      const int start = before + incl - tiles;
+      if (e < E && mt >= start && mt < start + tiles) {
+        tinfo[0] = e;
+        tinfo[1] = mt - start;
+      }
+      before += __shfl(incl, 63, 64);
+    }
+  }
+  __syncthreads();
+  const int e = tinfo[0];
+  if (e < 0) return;                                    // whole workgroup
+  const int64_t r0 = offsets[e] + (int64_t)tinfo[1] * MBM;
+  const int64_t r1 = offsets[e + 1] < r0 + MBM ? offsets[e + 1] : r0 + MBM;
+  const int64_t n0 = (int64_t)tn * MBN;
+  const int64_t rowbytes = K / 2;
+  const int64_t nrows = N - n0 < MBN ? N - n0 : MBN;
+  const auto ra = make_rsrc(x8, T * K);
+  const auto rb = make_rsrc(reinterpret_cast<const uint8_t*>(wq) + ((int64_t)e * N + n0) * rowbytes, nrows * rowbytes);
+  const int64_t G = K / 128;
+
+  // A: 4 DMA instructions per wave, 8 gathered rows each, 16-byte chunks
+  // XOR-swizzled by row; rows past the expert's end read as zeros.
+  uint32_t a_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int r = 8 * (wave * 4 + i) + (lane >> 3);
+    const int c = (lane & 7) ^ (r & 7);
+    const int64_t gr = r0 + r;
+    if (gr < r1) {
+      const int64_t tok = row_token ? row_token[gr] : gr;
+      a_off[i] = (uint32_t)(tok * K) + 16 * c;
+    } else {
+      a_off[i] = 0x80000000u;
+    }
+  }
+  // B: 2 DMA instructions per wave, 16 rows of 64 bytes each
+  uint32_t b_off[2];
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    const int r = 16 * (wave * 2 + i) + (lane >> 2);
+    b_off[i] = (uint32_t)(r * rowbytes) + 16 * (lane & 3);
+  }
+  auto issue = [&](int stage, int64_t k0) {
+    uint8_t* A = lds + stage * MSTAGE;
+    uint8_t* B = A + MA_TILE;
+#pragma unroll
+    for (int i = 0; i < 4; i++) lds_dma16(ra, A + (wave * 4 + i) * 1024, a_off[i] + (uint32_t)k0);
+#pragma unroll
+    for (int i = 0; i < 2; i++) lds_dma16(rb, B + (wave * 2 + i) * 1024, b_off[i] + (uint32_t)(k0 / 2));
+  };
+
+  // group scales of this lane's two columns, prefetched one step ahead as raw codes
+  const uint8_t* s8row[2];
+#pragma unroll
+  for (int j = 0; j < 2; j++) {
+    int64_t n = n0 + wn * 64 + 32 * j + l32;
+    n = n < N ? n : N - 1;
+    s8row[j] = s8 + ((int64_t)e * N + n) * G;
+  }
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
+
+  const int nk = (int)(K / MBK);
+  uint32_t ns[2];
+  issue(0, 0);
+#pragma unroll
+  for (int j = 0; j < 2; j++) ns[j] = s8row[j][0];
+
+  for (int kt = 0; kt < nk; kt++) {
+    const int stage = kt & 1;
+    wait_vm<0>();
+    __syncthreads();
+    Lut L[2];
+#pragma unroll
+    for (int j = 0; j < 2; j++) L[j] = make_lut(ns[j]);
+    if (kt + 1 < nk) {
+      issue(stage ^ 1, (int64_t)(kt + 1) * MBK);
+#pragma unroll
+      for (int j = 0; j < 2; j++) ns[j] = s8row[j][kt + 1];
+    }
+    const uint8_t* A = lds + stage * MSTAGE;
+    const uint8_t* B = A + MA_TILE;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; s2++) {
+      i32x8_t bf[2];
+#pragma unroll
+      for (int j = 0; j < 2; j++) {
+        const u32x4_t pw = ld16(B + (wn * 64 + 32 * j + l32) * 64 + 32 * s2 + 16 * h);
+        uint32_t d[8];
+#pragma unroll
+        for (int q = 0; q < 4; q++) lut_word(pw[q], L[j], d[2 * q], d[2 * q + 1]);
+        bf[j] = i32x8_t{(int)d[0], (int)d[1], (int)d[2], (int)d[3], (int)d[4], (int)d[5], (int)d[6], (int)d[7]};
+      }
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int r = wm * 128 + 32 * i + l32;
+        const int c0 = 4 * s2 + 2 * h;
+        const u32x4_t p0 = ld16(A + r * 128 + ((c0 ^ (r & 7)) << 4));
+        const u32x4_t p1 = ld16(A + r * 128 + (((c0 + 1) ^ (r & 7)) << 4));
+        const i32x8_t af = i32x8_t{(int)p0[0], (int)p0[1], (int)p0[2], (int)p0[3],
+                                   (int)p1[0], (int)p1[1], (int)p1[2], (int)p1[3]};
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf[j], acc[i][j], 0, 0, 0, 127, 0, 127);
+      }
+    }
+  }
+
+  // epilogue: C element r of a 32x32 tile sits at row 8*(r/4) + 4*h + r%4, col l32
+#pragma unroll
+  for (int j = 0; j < 2; j++) {
+    const int64_t col = n0 + wn * 64 + 32 * j + l32;
+    if (col >= N) continue;
+    const float cs = ch[(int64_t)e * N + col];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int64_t gr = r0 + wm * 128 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (gr < r1) {
+          const int64_t tok = row_token ? row_token[gr] : gr;
+          y[gr * N + col] = (uint16_t)f32_to_bf16_bits(acc[i][j][r] * (a_scale[tok] * cs));
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+wq_status wq_moe_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* ids, float* weights,
+                       int32_t* offsets, int32_t* row_token, int32_t* row_slot, void* stream) {
+  if (T < 0 || E < 1 || E > 64 || k < 1 || k > E) return WQ_EINVAL;
+  if (T * k > 0x7FFFFFFFLL) return WQ_EINVAL;
+  if (!offsets || (T > 0 && (!logits || !ids || !weights || !row_token || !row_slot))) return WQ_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  if (T > 0) k_route<<<(unsigned)((T + 3) / 4), 256, 0, s>>>(logits, T, E, k, ids, weights);
+  k_group<<<(unsigned)E, 1024, 0, s>>>(ids, T, E, k, offsets, row_token, row_slot);
+  return wq_launch_status();
+}
+
+wq_status wq_w4a8_prepack(const uint32_t* wq, const uint16_t* scales, int64_t experts, int64_t N, int64_t K,
+                          uint32_t* wq_out, uint8_t* s8, float* ch, void* stream) {
+  if (experts < 1 || N < 1 || K < 128 || K % 128) return WQ_EINVAL;
+  if (!wq || !scales || !wq_out || !s8 || !ch) return WQ_EINVAL;
+  if (!wq_aligned(wq) || !wq_aligned(wq_out)) return WQ_EALIGN;
+  if (!wq_numel_ok(experts * N, K)) return WQ_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t rows = experts * N, G = K / 128, words = rows * (K / 8);
+  k_w4a8_scales<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(scales, rows, (int)G, s8, ch);
+  k_w4a8_relayout<<<(unsigned)((words / 4 + 255) / 256), 256, 0, s>>>(wq, wq_out, words);
+  return wq_launch_status();
+}
+
+wq_status wq_w4a8_dequant(const uint32_t* wq, const uint8_t* s8, int64_t N, int64_t K, uint8_t* codes, void* stream) {
+  if (N < 1 || K < 128 || K % 128 || !wq || !s8 || !codes) return WQ_EINVAL;
+  if (!wq_numel_ok(N, K)) return WQ_EINVAL;
+  const int64_t words = N * (K / 8);
+  k_w4a8_dequant<<<(unsigned)((words + 255) / 256), 256, 0, (hipStream_t)stream>>>(wq, s8, N, K, codes);
+  return wq_launch_status();
+}
+
+wq_status wq_moe_gemm_w4a8(const uint8_t* x8, int64_t T, const float* a_scale, const int32_t* row_token, int64_t R,
+                           const int32_t* offsets, int32_t experts, int64_t N, int64_t K, const uint32_t* wq,
+                           const uint8_t* s8, const float* ch, uint16_t* y, void* stream) {
+  if (T < 1 || R < 0 || experts < 1 || N < 1 || K < 128 || K % 128) return WQ_EINVAL;
+  if (!x8 || !a_scale || !offsets || !wq || !s8 || !ch || (R > 0 && !y)) return WQ_EINVAL;
+  if (!row_token && R != T) return WQ_EINVAL;
+  if (!wq_aligned(x8) || !wq_aligned(wq)) return WQ_EALIGN;
+  if (T * K > 0x7FFFFFF0LL || (int64_t)MBN * K / 2 > 0x7FFFFFF0LL || R > 0x7FFFFFFFLL) return WQ_EINVAL;
+  if (R == 0) return WQ_OK;
+  static bool done[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return WQ_EHIP;
+  if (dev < 0 || dev >= 64 || !done[dev]) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(k_moe_gemm), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            MLDS) != hipSuccess)
+      return WQ_EHIP;
+    if (dev >= 0 && dev < 64) done[dev] = true;
+  }
+  const int64_t tiles_m = (R + MBM - 1) / MBM + experts;   // each expert adds at most one partial tile
+  const int64_t tiles_n = (N + MBN - 1) / MBN;
+  if (tiles_m * tiles_n > 0x7FFFFFFFLL) return WQ_EINVAL;
+  k_moe_gemm<<<(unsigned)(tiles_m * tiles_n), 512, MLDS, (hipStream_t)stream>>>(
+      x8, T, a_scale, row_token, offsets, experts, N, K, wq, s8, ch, y, (int)tiles_n);
+  return wq_launch_status();
+}
+
+}  // extern "C"
