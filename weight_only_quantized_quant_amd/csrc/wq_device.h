@@ -201,4 +201,11 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Workgroup barrier for the pipelined GEMM loops, without the memory fence of
+// __syncthreads(): that fence would also wait for the tile loads just issued
+// for later steps.  The waits the pipeline needs are explicit (vmcnt for this
+// wave's tile loads before the call, and here lgkmcnt for its LDS reads), and
+// the memory clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void tile_barrier() { __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 }  // namespace wq

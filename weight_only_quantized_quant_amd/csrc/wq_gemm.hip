@@ -209,25 +209,34 @@ __global__ __launch_bounds__(512) void k_gemv(const uint16_t* __restrict__ x, in
 // Prefill GEMM, 8-wave form
 // ---------------------------------------------------------------------------
 // 256x256 output tile per workgroup of 8 waves (2 along M x 4 along N, each
-// 128x64 with MFMA 32x32x16 bf16), K step 64, two LDS stages.  Two waves share
+// 128x64 with MFMA 32x32x16 bf16), K step 64, three LDS stages.  Two waves share
 // each SIMD, so one wave's MFMAs overlap the other's dequantization and LDS
-// reads.  Tiles arrive by direct-to-LDS buffer loads issued one K step ahead;
+// reads.  Tiles arrive by direct-to-LDS buffer loads issued two K steps ahead;
 // one barrier per step both publishes the step's tiles and retires the reads
 // of the stage the next loads overwrite.  x rows are 128 bytes in LDS with
 // their 16-byte chunks XOR-swizzled by row (chunk c of row r sits at c ^ (r & 7)),
-// which keeps the 32 lanes reading 32 rows of one chunk on distinct banks.
+// which keeps the 32 lanes reading 32 rows of one chunk on distinct banks; W
+// rows are swizzled the same way at their 16-byte chunk granularity.
 // Rows past M or N read as zeros through the buffer range; their results are
 // not stored.
 template <int WDT>
 struct Gemm8 {
   static constexpr int BM = 256, BN = 256, BK = 64;
+  static constexpr int NSTAGE = 3;                              // loads run NSTAGE - 1 steps ahead
   static constexpr int wbytes = BK * WTraits<WDT>::bits / 8;   // packed bytes per W row per step
   static constexpr int A_TILE = BM * BK * 2;                    // 32 KB
   static constexpr int B_TILE = BN * wbytes;                    // 8 KB (4-bit) or 16 KB (8-bit)
   static constexpr int STAGE = A_TILE + B_TILE;
-  static constexpr int LDS = 2 * STAGE;
+  static constexpr int LDS = NSTAGE * STAGE;
   static constexpr int B_DMA = B_TILE / 1024 / 8;               // 1 KB DMA instructions per wave
+  static constexpr int LPR = wbytes / 16;                       // 16-byte chunks per W row
+  // vector-memory instructions one step issues per lane: tile DMAs, then scales
+  static constexpr int VM_STEP = 4 + B_DMA + (WTraits<WDT>::bits == 4 ? 2 : 0);
 };
+// W rows of 32 or 64 bytes: chunk c of row r sits at c ^ bswz(r), which spreads
+// 8 consecutive rows read at one chunk over distinct banks.
+template <int LPR>
+__device__ __forceinline__ int bswz(int r) { return LPR == 2 ? (r >> 2) & 1 : (r >> 1) & 3; }
 
 template <int WDT>
 __global__ __launch_bounds__(512) void k_gemm8(const uint16_t* __restrict__ x, int64_t M, int64_t N, int64_t K,
@@ -261,13 +270,13 @@ __global__ __launch_bounds__(512) void k_gemm8(const uint16_t* __restrict__ x, i
     const int c = (lane & 7) ^ (r & 7);
     a_off[i] = (uint32_t)r * (uint32_t)(K * 2) + 16 * c;
   }
-  // B: rows of wbytes, lanes in row order.
-  constexpr int LPR = C::wbytes / 16;                          // lanes per W row
+  // B: rows of wbytes, lanes in row order, chunks swizzled by row.
+  constexpr int LPR = C::LPR;
   uint32_t b_off[C::B_DMA];
 #pragma unroll
   for (int i = 0; i < C::B_DMA; i++) {
     const int r = (1024 / C::wbytes) * (wave * C::B_DMA + i) + lane / LPR;
-    b_off[i] = (uint32_t)(r * rowbytes) + 16 * (lane % LPR);
+    b_off[i] = (uint32_t)(r * rowbytes) + 16 * ((lane % LPR) ^ bswz<LPR>(r));
   }
   auto issue = [&](int stage, int64_t k0) {
     uint8_t* A = lds + stage * C::STAGE;
@@ -314,37 +323,52 @@ __global__ __launch_bounds__(512) void k_gemm8(const uint16_t* __restrict__ x, i
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
 
+  // Step k's loads form group k (C::VM_STEP instructions per lane), issued two
+  // steps ahead into stage k % 3.  The loop is unrolled by two so that the raw
+  // scales of step k + 2 land in the registers step k has just converted: a
+  // register copy of a pending load would make the wave wait for all loads.
+  static_assert(C::NSTAGE == 3, "two steps of prefetch");
   const int nk = (int)(K / C::BK);
-  float cs[2];
-  uint32_t ns[2];
+  uint32_t nsa[2], nsb[2] = {0u, 0u};
   issue(0, 0);
 #pragma unroll
-  for (int j = 0; j < 2; j++) ns[j] = scale_raw(j, 0);
+  for (int j = 0; j < 2; j++) nsa[j] = scale_raw(j, 0);
+  if (nk > 1) {
+    issue(1, C::BK);
+#pragma unroll
+    for (int j = 0; j < 2; j++) nsb[j] = scale_raw(j, C::BK);
+  }
 
-  for (int kt = 0; kt < nk; kt++) {
-    const int stage = kt & 1;
-    // this wave's loads of step kt are in LDS; the barrier makes every wave's
-    // visible and guarantees stage ^ 1 is no longer being read
-    wait_vm<0>();
-    __syncthreads();
+  int stage = 0;
+  auto step = [&](int kt, uint32_t (&ns)[2]) {
+    // group kt has landed for this wave (group kt + 1 may still be in flight);
+    // the barrier makes every wave's visible and guarantees that the stage the
+    // next group overwrites (read in step kt - 1) is no longer being read
+    if (kt + 1 < nk) wait_vm<C::VM_STEP>();
+    else wait_vm<0>();
+    tile_barrier();
+    float cs[2];
 #pragma unroll
     for (int j = 0; j < 2; j++) cs[j] = scale_val(ns[j]);
-    if (kt + 1 < nk) {
-      issue(stage ^ 1, (int64_t)(kt + 1) * C::BK);
+    if (kt + 2 < nk) {
+      issue(stage == 0 ? 2 : stage - 1, (int64_t)(kt + 2) * C::BK);
 #pragma unroll
-      for (int j = 0; j < 2; j++) ns[j] = scale_raw(j, (int64_t)(kt + 1) * C::BK);
+      for (int j = 0; j < 2; j++) ns[j] = scale_raw(j, (int64_t)(kt + 2) * C::BK);
     }
     const uint8_t* A = lds + stage * C::STAGE;
     const uint8_t* B = A + C::A_TILE;
+    stage = stage == 2 ? 0 : stage + 1;
     bf16x8_t bq[2][4];
 #pragma unroll
     for (int j = 0; j < 2; j++) {
-      const uint8_t* bp = B + (wn * 64 + 32 * j + l32) * C::wbytes;
+      const int br = wn * 64 + 32 * j + l32;
+      const uint8_t* bp = B + br * C::wbytes;
+      const int sw = bswz<LPR>(br);
       if constexpr (WTraits<WDT>::bits == 4) {
-        dequant16<WDT>(ld16(bp + 16 * h), cs[j], bq[j]);
+        dequant16<WDT>(ld16(bp + 16 * (h ^ sw)), cs[j], bq[j]);
       } else {
-        dequant16<WDT>(ld16(bp + 32 * h), 1.0f, bq[j]);
-        dequant16<WDT>(ld16(bp + 32 * h + 16), 1.0f, bq[j] + 2);
+        dequant16<WDT>(ld16(bp + 16 * ((2 * h) ^ sw)), 1.0f, bq[j]);
+        dequant16<WDT>(ld16(bp + 16 * ((2 * h + 1) ^ sw)), 1.0f, bq[j] + 2);
       }
     }
 #pragma unroll
@@ -361,6 +385,10 @@ __global__ __launch_bounds__(512) void k_gemm8(const uint16_t* __restrict__ x, i
         for (int j = 0; j < 2; j++)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bq[j][s4], acc[i][j], 0, 0, 0);
     }
+  };
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(kt, nsa);
+    if (kt + 1 < nk) step(kt + 1, nsb);
   }
 
   // epilogue: C element r of a 32x32 tile sits at row 8*(r/4) + 4*h + r%4, col l32

@@ -21,8 +21,9 @@
 // one mask then give four table indices in k order.
 //
 // Grouped GEMM: 256 x 256 tiles of (rows of one expert) x (output channels),
-// 8 waves of 128 x 64, K step 128 = one INT4 group, two LDS stages filled by
-// direct-to-LDS loads; the activation rows are gathered through row_token.
+// 8 waves of 128 x 64, K step 128 = one INT4 group, three LDS stages filled by
+// direct-to-LDS loads two steps ahead; the activation rows are gathered through
+// row_token.
 // v_mfma_scale_f32_32x32x64_f8f6f4 with neutral block scales multiplies the
 // E4M3 operands; the epilogue applies the per-token and per-channel fp32
 // scales and rounds to bf16 once.  The fp8 MFMA treats E4M3 subnormal
@@ -215,7 +216,10 @@ constexpr int MBM = 256, MBN = 256, MBK = 128;
 constexpr int MA_TILE = MBM * MBK;                      // 32 KB of E4M3 rows
 constexpr int MB_TILE = MBN * MBK / 2;                  // 16 KB of packed INT4
 constexpr int MSTAGE = MA_TILE + MB_TILE;
-constexpr int MLDS = 2 * MSTAGE;                        // 96 KB
+constexpr int MNSTAGE = 3;                              // loads run two steps ahead
+constexpr int MLDS = MNSTAGE * MSTAGE;                  // 144 KB
+// W rows of 64 bytes: chunk c of row r sits at c ^ ((r >> 1) & 3)
+__device__ __forceinline__ int mbswz(int r) { return (r >> 1) & 3; }
 
 __global__ __launch_bounds__(512) void k_moe_gemm(const uint8_t* __restrict__ x8, int64_t T,
                                                   const float* __restrict__ a_scale,
@@ -226,6 +230,7 @@ __global__ __launch_bounds__(512) void k_moe_gemm(const uint8_t* __restrict__ x8
                                                   int tiles_n) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ int tinfo[2];
+  __shared__ float rscale[MBM];                         // a_scale of each row of the tile
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
@@ -268,6 +273,10 @@ __global__ __launch_bounds__(512) void k_moe_gemm(const uint8_t* __restrict__ x8
   const auto ra = make_rsrc(x8, T * K);
   const auto rb = make_rsrc(reinterpret_cast<const uint8_t*>(wq) + ((int64_t)e * N + n0) * rowbytes, nrows * rowbytes);
   const int64_t G = K / 128;
+  if (tid < MBM) {
+    const int64_t gr = r0 + tid;
+    rscale[tid] = gr < r1 ? a_scale[row_token ? row_token[gr] : gr] : 0.0f;
+  }
 
   // A: 4 DMA instructions per wave, 8 gathered rows each, 16-byte chunks
   // XOR-swizzled by row; rows past the expert's end read as zeros.
@@ -284,12 +293,12 @@ __global__ __launch_bounds__(512) void k_moe_gemm(const uint8_t* __restrict__ x8
       a_off[i] = 0x80000000u;
     }
   }
-  // B: 2 DMA instructions per wave, 16 rows of 64 bytes each
+  // B: 2 DMA instructions per wave, 16 rows of 64 bytes each, chunks swizzled
   uint32_t b_off[2];
 #pragma unroll
   for (int i = 0; i < 2; i++) {
     const int r = 16 * (wave * 2 + i) + (lane >> 2);
-    b_off[i] = (uint32_t)(r * rowbytes) + 16 * (lane & 3);
+    b_off[i] = (uint32_t)(r * rowbytes) + 16 * ((lane & 3) ^ mbswz(r));
   }
   auto issue = [&](int stage, int64_t k0) {
     uint8_t* A = lds + stage * MSTAGE;
@@ -300,7 +309,7 @@ __global__ __launch_bounds__(512) void k_moe_gemm(const uint8_t* __restrict__ x8
     for (int i = 0; i < 2; i++) lds_dma16(rb, B + (wave * 2 + i) * 1024, b_off[i] + (uint32_t)(k0 / 2));
   };
 
-  // group scales of this lane's two columns, prefetched one step ahead as raw codes
+  // group scales of this lane's two columns
   const uint8_t* s8row[2];
 #pragma unroll
   for (int j = 0; j < 2; j++) {
@@ -317,68 +326,106 @@ __global__ __launch_bounds__(512) void k_moe_gemm(const uint8_t* __restrict__ x8
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
 
-  const int nk = (int)(K / MBK);
-  uint32_t ns[2];
-  issue(0, 0);
+  // B operands of half s2 of a step (K 64): 32 E4M3 codes per lane and column
+  auto lut_half = [&](const uint8_t* B, int s2, const Lut (&L)[2], i32x8_t (&bf)[2]) {
 #pragma unroll
-  for (int j = 0; j < 2; j++) ns[j] = s8row[j][0];
+    for (int j = 0; j < 2; j++) {
+      const int br = wn * 64 + 32 * j + l32;
+      const u32x4_t pw = ld16(B + br * 64 + 16 * ((2 * s2 + h) ^ mbswz(br)));
+      uint32_t d[8];
+#pragma unroll
+      for (int q = 0; q < 4; q++) lut_word(pw[q], L[j], d[2 * q], d[2 * q + 1]);
+      bf[j] = i32x8_t{(int)d[0], (int)d[1], (int)d[2], (int)d[3], (int)d[4], (int)d[5], (int)d[6], (int)d[7]};
+    }
+  };
+  auto mfma_half = [&](const uint8_t* A, int s2, const i32x8_t (&bf)[2]) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int r = wm * 128 + 32 * i + l32;
+      const int c0 = 4 * s2 + 2 * h;
+      const u32x4_t p0 = ld16(A + r * 128 + ((c0 ^ (r & 7)) << 4));
+      const u32x4_t p1 = ld16(A + r * 128 + (((c0 + 1) ^ (r & 7)) << 4));
+      const i32x8_t af = i32x8_t{(int)p0[0], (int)p0[1], (int)p0[2], (int)p0[3],
+                                 (int)p1[0], (int)p1[1], (int)p1[2], (int)p1[3]};
+#pragma unroll
+      for (int j = 0; j < 2; j++)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf[j], acc[i][j], 0, 0, 0, 127, 0, 127);
+    }
+  };
 
+  // Software pipeline.  Step k's loads (group k) go to stage k % 3, two steps
+  // ahead.  At the top of step k groups <= k + 1 are resident and visible; the
+  // MFMAs of each half run on operands converted during the previous half, so
+  // the table lookups of one half overlap the matrix work of the other: half 0
+  // converts half 1 of step k, half 1 converts half 0 of step k + 1.  The
+  // barrier at the end of step k publishes group k + 2 and retires every read
+  // of stage k % 3, which step k + 1 then refills with group k + 3.
+  const int nk = (int)(K / MBK);
+  uint32_t sn[2], sn2[2] = {0u, 0u};                   // raw s8 of steps k + 1, k + 2
+  issue(0, 0);
+  uint32_t s0[2];
+#pragma unroll
+  for (int j = 0; j < 2; j++) s0[j] = s8row[j][0];
+  if (nk > 1) {
+    issue(1, MBK);
+#pragma unroll
+    for (int j = 0; j < 2; j++) sn[j] = s8row[j][1];
+  }
+  wait_vm<0>();
+  __syncthreads();                                      // also publishes rscale
+  Lut Lc[2];
+#pragma unroll
+  for (int j = 0; j < 2; j++) Lc[j] = make_lut(s0[j]);
+  i32x8_t bc[2], bn[2];
+  lut_half(lds + MA_TILE, 0, Lc, bc);
+
+  int stage = 0;
   for (int kt = 0; kt < nk; kt++) {
-    const int stage = kt & 1;
-    wait_vm<0>();
-    __syncthreads();
-    Lut L[2];
+    const int st1 = stage == 2 ? 0 : stage + 1;
+    const int st2 = st1 == 2 ? 0 : st1 + 1;
+    if (kt + 2 < nk) {
+      issue(st2, (int64_t)(kt + 2) * MBK);
 #pragma unroll
-    for (int j = 0; j < 2; j++) L[j] = make_lut(ns[j]);
-    if (kt + 1 < nk) {
-      issue(stage ^ 1, (int64_t)(kt + 1) * MBK);
-#pragma unroll
-      for (int j = 0; j < 2; j++) ns[j] = s8row[j][kt + 1];
+      for (int j = 0; j < 2; j++) sn2[j] = s8row[j][kt + 2];
     }
+    // (on the last step the second conversion reads a stale stage; unused)
     const uint8_t* A = lds + stage * MSTAGE;
-    const uint8_t* B = A + MA_TILE;
+    lut_half(A + MA_TILE, 1, Lc, bn);
+    mfma_half(A, 0, bc);
 #pragma unroll
-    for (int s2 = 0; s2 < 2; s2++) {
-      i32x8_t bf[2];
+    for (int j = 0; j < 2; j++) Lc[j] = make_lut(sn[j]);
+    lut_half(lds + st1 * MSTAGE + MA_TILE, 0, Lc, bc);
+    mfma_half(A, 1, bn);
+    wait_vm<0>();
+    tile_barrier();
 #pragma unroll
-      for (int j = 0; j < 2; j++) {
-        const u32x4_t pw = ld16(B + (wn * 64 + 32 * j + l32) * 64 + 32 * s2 + 16 * h);
-        uint32_t d[8];
-#pragma unroll
-        for (int q = 0; q < 4; q++) lut_word(pw[q], L[j], d[2 * q], d[2 * q + 1]);
-        bf[j] = i32x8_t{(int)d[0], (int)d[1], (int)d[2], (int)d[3], (int)d[4], (int)d[5], (int)d[6], (int)d[7]};
-      }
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int r = wm * 128 + 32 * i + l32;
-        const int c0 = 4 * s2 + 2 * h;
-        const u32x4_t p0 = ld16(A + r * 128 + ((c0 ^ (r & 7)) << 4));
-        const u32x4_t p1 = ld16(A + r * 128 + (((c0 + 1) ^ (r & 7)) << 4));
-        const i32x8_t af = i32x8_t{(int)p0[0], (int)p0[1], (int)p0[2], (int)p0[3],
-                                   (int)p1[0], (int)p1[1], (int)p1[2], (int)p1[3]};
-#pragma unroll
-        for (int j = 0; j < 2; j++)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf[j], acc[i][j], 0, 0, 0, 127, 0, 127);
-      }
-    }
+    for (int j = 0; j < 2; j++) sn[j] = sn2[j];
+    stage = st1;
   }
 
-  // epilogue: C element r of a 32x32 tile sits at row 8*(r/4) + 4*h + r%4, col l32
+  // epilogue: C element r of a 32x32 tile sits at row 8*(r/4) + 4*h + r%4, col l32.
+  // Stores go through a buffer range covering the tile's valid rows, so rows
+  // past the expert's end are dropped by the hardware and offsets stay 32-bit.
+  const auto ry = make_rsrc(y + r0 * N, (r1 - r0) * N * 2);
+  const uint32_t rowb = (uint32_t)(N * 2);
+  float cs[2];
+  uint32_t cb[2];
 #pragma unroll
   for (int j = 0; j < 2; j++) {
     const int64_t col = n0 + wn * 64 + 32 * j + l32;
-    if (col >= N) continue;
-    const float cs = ch[(int64_t)e * N + col];
+    cs[j] = col < N ? ch[(int64_t)e * N + col] : 0.0f;
+    cb[j] = col < N ? (uint32_t)(col * 2) : 0x80000000u;   // columns past N: out of range
+  }
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+  for (int i = 0; i < 4; i++) {
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int64_t gr = r0 + wm * 128 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (gr < r1) {
-          const int64_t tok = row_token ? row_token[gr] : gr;
-          y[gr * N + col] = (uint16_t)f32_to_bf16_bits(acc[i][j][r] * (a_scale[tok] * cs));
-        }
-      }
+    for (int r = 0; r < 16; r++) {
+      const int lr = wm * 128 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+      const float rs = rscale[lr];
+      const uint32_t pr = pack_bf16x2(acc[i][0][r] * (rs * cs[0]), acc[i][1][r] * (rs * cs[1]));
+      const uint32_t off = (uint32_t)lr * rowb;
+      __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(pr & 0xFFFFu), ry, (int)(off + cb[0]), 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(pr >> 16), ry, (int)(off + cb[1]), 0, 0);
     }
   }
 }
@@ -426,7 +473,11 @@ wq_status wq_moe_gemm_w4a8(const uint8_t* x8, int64_t T, const float* a_scale, c
   if (!x8 || !a_scale || !offsets || !wq || !s8 || !ch || (R > 0 && !y)) return WQ_EINVAL;
   if (!row_token && R != T) return WQ_EINVAL;
   if (!wq_aligned(x8) || !wq_aligned(wq)) return WQ_EALIGN;
-  if (T * K > 0x7FFFFFF0LL || (int64_t)MBN * K / 2 > 0x7FFFFFF0LL || R > 0x7FFFFFFFLL) return WQ_EINVAL;
+  // 32-bit buffer offsets: the activations, one expert's 256-row W panel, one
+  // 256-row output tile
+  if (T * K > 0x7FFFFFF0LL || (int64_t)MBN * K / 2 > 0x7FFFFFF0LL || (int64_t)MBM * N * 2 > 0x7FFFFFF0LL ||
+      R > 0x7FFFFFFFLL)
+    return WQ_EINVAL;
   if (R == 0) return WQ_OK;
   static bool done[64] = {};
   int dev = 0;
