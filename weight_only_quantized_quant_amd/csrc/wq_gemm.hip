@@ -391,20 +391,29 @@ __global__ __launch_bounds__(512) void k_gemm8(const uint16_t* __restrict__ x, i
     if (kt + 1 < nk) step(kt + 1, nsb);
   }
 
-  // epilogue: C element r of a 32x32 tile sits at row 8*(r/4) + 4*h + r%4, col l32
+  // epilogue: C element r of a 32x32 tile sits at row 8*(r/4) + 4*h + r%4, col l32.
+  // Stores go through a buffer range covering the tile's rows below M, so the
+  // rest are dropped by the hardware and offsets stay 32-bit.
+  const auto ry = make_rsrc(y + m0 * N, mrows * N * 2);
+  const uint32_t rowb = (uint32_t)(N * 2);
+  float cs[2];
+  uint32_t cb[2];
 #pragma unroll
   for (int j = 0; j < 2; j++) {
     const int64_t col = n0 + wn * 64 + 32 * j + l32;
-    if (col >= N) continue;
-    float cscale = 1.0f;
-    if constexpr (WDT == W_FP8) cscale = chscale[col];
+    cs[j] = 1.0f;
+    if constexpr (WDT == W_FP8) cs[j] = col < N ? chscale[col] : 0.0f;
+    cb[j] = col < N ? (uint32_t)(col * 2) : 0x80000000u;    // columns past N: out of range
+  }
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+  for (int i = 0; i < 4; i++) {
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int64_t row = m0 + wm * 128 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (row < M) y[row * N + col] = (uint16_t)f32_to_bf16_bits(acc[i][j][r] * cscale);
-      }
+    for (int r = 0; r < 16; r++) {
+      const uint32_t lr = (uint32_t)(wm * 128 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3));
+      const uint32_t pr = pack_bf16x2(acc[i][0][r] * cs[0], acc[i][1][r] * cs[1]);
+      const uint32_t off = lr * rowb;
+      __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(pr & 0xFFFFu), ry, (int)(off + cb[0]), 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(pr >> 16), ry, (int)(off + cb[1]), 0, 0);
     }
   }
 }
@@ -662,8 +671,8 @@ template <int WDT>
 wq_status launch_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w, const void* sc, int group,
                       const float* ch, uint16_t* y, hipStream_t s) {
   using C8 = Gemm8<WDT>;
-  // 32-bit buffer offsets: one 256-row x tile and one 256-row W tile
-  if ((int64_t)C8::BM * K * 2 > 0x7FFFFFF0LL) return WQ_EINVAL;
+  // 32-bit buffer offsets: one 256-row x tile, one 256-row W tile, one 256-row y tile
+  if ((int64_t)C8::BM * K * 2 > 0x7FFFFFF0LL || (int64_t)C8::BM * N * 2 > 0x7FFFFFF0LL) return WQ_EINVAL;
   if (allow_lds<k_gemm8<WDT>>(C8::LDS) != hipSuccess) return WQ_EHIP;
   const int tm = (int)((M + C8::BM - 1) / C8::BM), tn = (int)((N + C8::BN - 1) / C8::BN);
   const int gshift = group == 32 ? 5 : group == 64 ? 6 : 7;
