@@ -16,12 +16,14 @@ The same JSON line carries the roofline of that kernel (HIP events over the
 timed region on the launch stream), the oracle timed on the host (`cpu_baseline`)
 and `secondary` measurements: decode at M = 4 and 16, W8A16, prefill MXFP4 at
 M = 8192 (TFLOP/s), the activation quantizers at 4096 x 7168, the MXFP4 weight
-quantizer, a streaming copy and torch.matmul (hipBLASLt) at the prefill shape
-as secondary denominators.
+quantizer, the W4A8 mixture-of-experts grouped GEMMs (gate/up and down, with
+routing, token quantization and prepack), a streaming copy and torch.matmul
+(hipBLASLt) at the prefill shape as secondary denominators.
 
 --only CASE runs a single case without the full summary (for rocprofv3):
 decode (the same graph-timed steps as the headline, prints one short JSON
-line), decode_w8, prefill, quant_e4m3, quant_mxfp4, wquant_mxfp4, copy.
+line), decode_w8, prefill, quant_e4m3, quant_mxfp4, wquant_mxfp4, copy,
+moe_gate_up, moe_down.
 """
 from __future__ import annotations
 
@@ -39,6 +41,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 ROTATE_BYTES = 700e6           # > 2.5x the 256 MB Infinity Cache
 
 
@@ -236,6 +239,43 @@ class WeightQuant:
         self.W.quantize_mxfp4(self.w[i % 2], 32, codes=c, scales=s)
 
 
+class MoeW4A8:
+    """W4A8 mixture-of-experts grouped GEMM: 64 experts, top-8 routing of 4096
+    tokens, hidden 4096, expert intermediate 1536.  which = "gate_up" (rows
+    gathered by token, N = 3072, K = 4096) or "down" (grouped rows, N = 4096,
+    K = 1536).  INT4 group-128 weights quantized on the GPU from device-side
+    N(0, 0.02) weights, then prepacked; per-token E4M3 activations."""
+
+    def __init__(self, torch, W, which):
+        from synthetic import moe_down_input_gpu, moe_expert_weight_gpu, moe_router_logits, moe_tokens
+        E, T, k, inter, hidden = 64, 4096, 8, 1536, 4096
+        self.W, self.which = W, which
+        self.N, self.K = (2 * inter, hidden) if which == "gate_up" else (hidden, inter)
+        self.logits = torch.from_numpy(moe_router_logits(0)).cuda()
+        _, _, self.off, rt, _ = W.wq_moe_route(self.logits, k)
+        if which == "gate_up":
+            self.x = dev_bf16(torch, moe_tokens())
+            self.rt = rt
+        else:
+            self.x = moe_down_input_gpu(rows=T * k, inter=inter)
+            self.rt = None
+        self.x8, a = W.quantize_e4m3(self.x, -1)
+        self.a = a.reshape(-1).contiguous()
+        self.packed = torch.empty((E, self.N, self.K // 8), dtype=torch.int32, device="cuda")
+        self.sb = torch.empty((E, self.N, self.K // 128), dtype=torch.bfloat16, device="cuda")
+        for e in range(E):
+            W.quantize_int4(moe_expert_weight_gpu(e, which, hidden=hidden, inter=inter), 128,
+                            packed=self.packed[e], scales=self.sb[e])
+        self.wq, self.s8, self.ch = W.wq_w4a8_prepack(self.packed, self.sb)
+        self.R = T * k
+        self.y = torch.empty((self.R, self.N), dtype=torch.bfloat16, device="cuda")
+        self.flops = 2.0 * self.R * self.N * self.K
+        self.k = k
+
+    def launch(self, i):
+        self.W.wq_moe_gemm_w4a8(self.x8, self.a, self.rt, self.off, self.wq, self.s8, self.ch, y=self.y)
+
+
 class Copy:
     """Streaming copy of 256 MiB (read + write) as a secondary HBM denominator."""
 
@@ -296,9 +336,10 @@ def main():
         mk = {"decode_w8": lambda: Decode(torch, W, 1, "e4m3"),
               "prefill": lambda: Prefill(torch, W), "quant_e4m3": lambda: ActQuant(torch, W, "e4m3"),
               "quant_mxfp4": lambda: ActQuant(torch, W, "mxfp4"), "copy": lambda: Copy(torch),
-              "wquant_mxfp4": lambda: WeightQuant(torch, W)}[case]
+              "wquant_mxfp4": lambda: WeightQuant(torch, W),
+              "moe_gate_up": lambda: MoeW4A8(torch, W, "gate_up"), "moe_down": lambda: MoeW4A8(torch, W, "down")}[case]
         obj = mk()
-        reps = args.reps or (10 if case == "prefill" else 100)
+        reps = args.reps or (10 if case in ("prefill", "moe_gate_up", "moe_down") else 100)
         for i in range(reps):
             obj.launch(i)
         torch.cuda.synchronize()
@@ -368,6 +409,22 @@ def main():
     secondary["weight_quant_mxfp4_14336x4096_fp32"] = {"GB/s": round(wq_.bytes / (t * 1e-3) / 1e9, 1),
                                                        "us": round(t * 1e3, 2)}
     del wq_
+    for which in ("gate_up", "down"):
+        mo = MoeW4A8(torch, W, which)
+        t = time_eager(torch, mo.launch, 10)
+        tf = mo.flops / (t * 1e-3) / 1e12
+        secondary[f"moe_w4a8_{which}_64x{mo.N}x{mo.K}_top8"] = {
+            "TFLOP/s": round(tf, 1), "frac_fp8_mfma": round(tf / FP8_PEAK_TFLOPS, 4), "us": round(t * 1e3, 1),
+            "flops": mo.flops}
+        if which == "gate_up":
+            t = time_eager(torch, lambda i: W.wq_moe_route(mo.logits, mo.k), 20)
+            secondary["moe_route_4096x64_top8"] = {"us": round(t * 1e3, 2)}
+            t = time_eager(torch, lambda i: W.quantize_e4m3(mo.x, -1), 20)
+            secondary["moe_token_quant_e4m3_4096x4096"] = {"us": round(t * 1e3, 2)}
+        t = time_eager(torch, lambda i: W.wq_w4a8_prepack(mo.packed, mo.sb, wq_out=mo.wq), 5)
+        secondary[f"moe_w4a8_prepack_{which}"] = {"us": round(t * 1e3, 1)}
+        del mo
+        torch.cuda.empty_cache()
     cp = Copy(torch)
     t = time_eager(torch, cp.launch, 20)
     secondary["stream_copy_256MiB"] = {"GB/s": round(cp.bytes / (t * 1e-3) / 1e9, 1)}
