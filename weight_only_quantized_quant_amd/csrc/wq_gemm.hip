@@ -74,11 +74,23 @@ __device__ __forceinline__ void dequant16(u32x4_t w, float s, bf16x8_t out[4]) {
 // ---------------------------------------------------------------------------
 // Decode GEMV
 // ---------------------------------------------------------------------------
+// Scales loaded ahead of use are kept as raw bits and converted at the use:
+// converting next to the load would make the wave wait for it there.
+template <int WDT>
+__device__ __forceinline__ uint32_t scale_raw_of(__amdgpu_buffer_rsrc_t r, uint32_t idx) {
+  if constexpr (WDT == W_INT4) return __builtin_amdgcn_raw_buffer_load_b16(r, (int)(idx * 2), 0, 0);
+  else if constexpr (WDT == W_FP4) return __builtin_amdgcn_raw_buffer_load_b8(r, (int)idx, 0, 0);
+  else return 0u;
+}
+template <int WDT>
+__device__ __forceinline__ float scale_from_raw(uint32_t raw) {
+  if constexpr (WDT == W_INT4) return bf16_to_f32(raw);
+  else if constexpr (WDT == W_FP4) return e8m0_as_scale(raw);
+  else return 1.0f;
+}
 template <int WDT>
 __device__ __forceinline__ float scale_of(__amdgpu_buffer_rsrc_t r, uint32_t idx) {
-  if constexpr (WDT == W_INT4) return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, (int)(idx * 2), 0, 0));
-  else if constexpr (WDT == W_FP4) return e8m0_as_scale(__builtin_amdgcn_raw_buffer_load_b8(r, (int)idx, 0, 0));
-  else return 1.0f;
+  return scale_from_raw<WDT>(scale_raw_of<WDT>(r, idx));
 }
 
 // XLDS (M <= 4): each wave stages the x rows of its own K chunk in a private
@@ -488,7 +500,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_ring(const uint16_t* __restric
   //    thinner slices every lane loads its own per-step scales instead (a 16-byte
   //    window could leave the buffer range at the last row and read as zeros).
   const bool sdma = sbrow >= 16;
-  float svr[SPW];
+  uint32_t svr[SPW];
   if constexpr (WDT != W_FP8) {
     if (sdma) {
       const int cpr = (int)srs / 16;
@@ -497,7 +509,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_ring(const uint16_t* __restric
     } else {
 #pragma unroll
       for (int c = 0; c < SPW; c++)
-        svr[c] = scale_of<WDT>(rs, (uint32_t)nl * spr + ((kbase + c * KSTEP + EPL * g) >> gs));
+        svr[c] = scale_raw_of<WDT>(rs, (uint32_t)nl * spr + ((kbase + c * KSTEP + EPL * g) >> gs));
     }
   }
   // 2) x rows of the slice, 1 KB per DMA instruction
@@ -535,10 +547,10 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_ring(const uint16_t* __restric
     float scv = 1.0f;
     if constexpr (WDT == W_INT4) {
       const uint32_t gi = (uint32_t)(c * KSTEP + EPL * g) >> gs;
-      scv = sdma ? bf16_to_f32(*reinterpret_cast<const uint16_t*>(sl + nl * srs + 2 * gi)) : svr[c];
+      scv = sdma ? bf16_to_f32(*reinterpret_cast<const uint16_t*>(sl + nl * srs + 2 * gi)) : scale_from_raw<WDT>(svr[c]);
     } else if constexpr (WDT == W_FP4) {
       const uint32_t gi = (uint32_t)(c * KSTEP + EPL * g) >> 5;
-      scv = sdma ? e8m0_as_scale(sl[nl * srs + gi]) : svr[c];
+      scv = sdma ? e8m0_as_scale(sl[nl * srs + gi]) : scale_from_raw<WDT>(svr[c]);
     }
     bf16x8_t xa[MF];
 #pragma unroll
@@ -605,11 +617,134 @@ void gemv_nstep(const GemvSplit& sp, const uint16_t* x, int64_t M, int64_t N, in
   }
 }
 
+// 4 < M <= 16: the 16 x rows of the wave's slice do not fit a wave's LDS
+// share, so each step's x chunk (16 rows x 128 or 64 k) travels through its
+// own ring next to the weights, fetched by direct-to-LDS loads (x is read from
+// L2 by every workgroup).  A row's 16-byte chunks are XOR-swizzled by the row
+// so that the 16 lanes reading one chunk of 16 rows use distinct banks; rows
+// >= M read as zeros.  Scales come from per-lane loads issued up front.
+template <int WDT, int SPW, int R, int NW>
+__global__ __launch_bounds__(64 * NW) void k_gemv_ring16(const uint16_t* __restrict__ x, int M, int64_t N,
+                                                    int64_t K, const uint8_t* __restrict__ w,
+                                                    const void* __restrict__ sc, int group_shift,
+                                                    const float* __restrict__ chscale, uint16_t* __restrict__ y) {
+  constexpr int EPL = WTraits<WDT>::bits == 4 ? 32 : 16;
+  constexpr int KSTEP = 4 * EPL;
+  constexpr int KSL = SPW * KSTEP;
+  constexpr int MF = EPL / 8;
+  constexpr int BPE2 = WTraits<WDT>::bits == 4 ? 1 : 2;
+  constexpr int XRB = KSTEP * 2;                              // bytes of one x row of a step
+  constexpr int XSLOT = 16 * XRB;                             // 4 KB or 2 KB
+  constexpr int XQ = XSLOT / 1024;                            // x DMA instructions per step
+  constexpr int RPI = 1024 / XRB;                             // x rows per DMA instruction
+  constexpr int CPR = XRB / 16;                               // 16-byte chunks per x row
+  constexpr int VMS = 1 + XQ;                                 // loads per step per lane
+  constexpr int SLOT = 1024 + XSLOT;
+  static_assert(R <= SPW && R == 2, "two-deep ring");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nl = lane & 15, g = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const uint32_t rowbytes = (uint32_t)(K * BPE2 / 2);
+  const int64_t nrows = N - n0 < 16 ? N - n0 : 16;
+  const int gs = WDT == W_INT4 ? group_shift : 5;
+  const uint32_t spr = (uint32_t)(K >> gs);
+  constexpr int SB = WDT == W_INT4 ? 2 : 1;
+  const auto rw = make_rsrc(w + n0 * rowbytes, nrows * rowbytes);
+  const auto rs = make_rsrc(reinterpret_cast<const uint8_t*>(sc) + (WDT == W_FP8 ? 0 : n0 * spr * SB),
+                            WDT == W_FP8 ? 0 : nrows * spr * SB);
+  const auto rx = make_rsrc(x, (int64_t)M * K * 2);
+  const uint32_t kbase = (uint32_t)(wave * KSL);
+  uint8_t* ring = smem + wave * (R * SLOT);
+
+  uint32_t svr[SPW];
+  if constexpr (WDT != W_FP8) {
+#pragma unroll
+    for (int c = 0; c < SPW; c++)
+      svr[c] = scale_raw_of<WDT>(rs, (uint32_t)nl * spr + ((kbase + c * KSTEP + EPL * g) >> gs));
+  }
+  const uint32_t wlane = (uint32_t)nl * rowbytes + (kbase + EPL * g) * BPE2 / 2;
+  uint32_t xoff[XQ];
+#pragma unroll
+  for (int q = 0; q < XQ; q++) {
+    const int r = q * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ (r & (CPR - 1));
+    xoff[q] = (uint32_t)(r * (uint32_t)K + kbase + 8 * c) * 2;
+  }
+  auto issue = [&](int slot, int step) {
+    uint8_t* b = ring + slot * SLOT;
+    lds_dma16(rw, b, wlane + step * KSTEP * BPE2 / 2);
+#pragma unroll
+    for (int q = 0; q < XQ; q++) lds_dma16(rx, b + 1024 + q * 1024, xoff[q] + step * KSTEP * 2);
+  };
+#pragma unroll
+  for (int c = 0; c < R; c++) issue(c, c);
+
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < SPW; c++) {
+    if (c + 1 < SPW) wait_vm<VMS>();
+    else wait_vm<0>();
+    const uint8_t* b = ring + (c % R) * SLOT;
+    const u32x4_t wv = ld16(b + lane * 16);
+    bf16x8_t xa[MF];
+#pragma unroll
+    for (int j = 0; j < MF; j++) {
+      const int ch = (EPL / 8) * g + j;
+      xa[j] = as_bf16x8(ld16(b + 1024 + nl * XRB + 16 * (ch ^ (nl & (CPR - 1)))));
+    }
+    const float scv = WDT == W_FP8 ? 1.0f : scale_from_raw<WDT>(svr[c]);
+    bf16x8_t bq[4];
+    dequant16<WDT>(wv, scv, bq);
+    if (c + R < SPW) {
+      // the slot's reads have returned before the refill may overwrite it
+      __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue(c % R, c + R);
+    }
+#pragma unroll
+    for (int j = 0; j < MF; j++) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[j], bq[j], acc, 0, 0, 0);
+  }
+
+  float* red = reinterpret_cast<float*>(smem);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; i++) red[(wave * 16 + 4 * g + i) * 16 + nl] = acc[i];
+  __syncthreads();
+  if (threadIdx.x < 256) {
+    const int m = threadIdx.x >> 4, n = threadIdx.x & 15;
+    const int64_t col = n0 + n;
+    if (m < M && col < N) {
+      float s = 0.0f;
+#pragma unroll
+      for (int wv = 0; wv < NW; wv++) s += red[(wv * 16 + m) * 16 + n];
+      if constexpr (WDT == W_FP8) s *= chscale[col];
+      y[(int64_t)m * N + col] = (uint16_t)f32_to_bf16_bits(s);
+    }
+  }
+}
+
 // Measured on MI355X for K = 4096: 4 waves per 16-column tile with a 2-deep
 // ring beat deeper rings (requests all in flight arrive in an order that
 // bunches the dequantization work at the end) and 8-wave splits.
 constexpr int RING_NW = 4;
 constexpr int RING_DEPTH = 2;
+template <int WDT, int SPW>
+wq_status ring16_go(int64_t M, const uint16_t* x, int64_t N, int64_t K, const uint8_t* w, const void* sc, int gshift,
+                    const float* ch, uint16_t* y, hipStream_t s) {
+  constexpr int R = SPW < 2 ? SPW : 2;
+  if constexpr (R < 2) {
+    return WQ_EUNSUPPORTED;
+  } else {
+    constexpr int XSLOT = 16 * 4 * (WTraits<WDT>::bits == 4 ? 32 : 16) * 2;
+    const size_t lds = (size_t)RING_NW * R * (1024 + XSLOT);
+    const unsigned grid = (unsigned)((N + 15) / 16);
+    if (allow_lds<k_gemv_ring16<WDT, SPW, R, RING_NW>>(lds) != hipSuccess) return WQ_EHIP;
+    k_gemv_ring16<WDT, SPW, R, RING_NW><<<grid, 64 * RING_NW, lds, s>>>(x, (int)M, N, K, w, sc, gshift, ch, y);
+    return WQ_OK;
+  }
+}
+
 template <int WDT, int SPW>
 wq_status ring_go(int64_t M, const uint16_t* x, int64_t N, int64_t K, const uint8_t* w, const void* sc, int gshift,
              const float* ch, uint16_t* y, hipStream_t s) {
@@ -648,6 +783,19 @@ wq_status launch_gemv(const uint16_t* x, int64_t M, int64_t N, int64_t K, const 
         case 4: st = ring_go<WDT, 4>(M, x, N, K, w, sc, gshift, ch, y, s); break;
         case 8: st = ring_go<WDT, 8>(M, x, N, K, w, sc, gshift, ch, y, s); break;
         default: st = ring_go<WDT, 16>(M, x, N, K, w, sc, gshift, ch, y, s); break;
+      }
+      return st != WQ_OK ? st : wq_launch_status();
+    }
+  }
+  if (M > 4 && M <= 16 && K % (KSTEP * RING_NW) == 0 && 16 * K * 2 <= 0x7FFFFFF0LL) {
+    const int64_t spw = K / (KSTEP * RING_NW);
+    if (spw == 2 || spw == 4 || spw == 8 || spw == 16) {
+      wq_status st;
+      switch (spw) {
+        case 2: st = ring16_go<WDT, 2>(M, x, N, K, w, sc, gshift, ch, y, s); break;
+        case 4: st = ring16_go<WDT, 4>(M, x, N, K, w, sc, gshift, ch, y, s); break;
+        case 8: st = ring16_go<WDT, 8>(M, x, N, K, w, sc, gshift, ch, y, s); break;
+        default: st = ring16_go<WDT, 16>(M, x, N, K, w, sc, gshift, ch, y, s); break;
       }
       return st != WQ_OK ? st : wq_launch_status();
     }
