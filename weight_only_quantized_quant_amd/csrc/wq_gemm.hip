@@ -335,54 +335,73 @@ __global__ __launch_bounds__(512) void k_gemm8(const uint16_t* __restrict__ x, i
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
 
-  // Step k's loads form group k (C::VM_STEP instructions per lane), issued two
-  // steps ahead into stage k % 3.  The loop is unrolled by two so that the raw
-  // scales of step k + 2 land in the registers step k has just converted: a
-  // register copy of a pending load would make the wave wait for all loads.
+  // Software pipeline.  Step k's loads (group k) go to stage k % 3, two steps
+  // ahead; at the top of step k groups <= k + 1 are resident and visible.  The
+  // MFMAs of step k run on W fragments converted during step k - 1, and each of
+  // its four k16 slices converts the matching quarter of step k + 1's fragments,
+  // so dequantization overlaps the matrix work inside the wave.  The barrier at
+  // the end of step k publishes group k + 2 and retires every read of stage
+  // k % 3, which step k + 1 refills with group k + 3.  The loop is unrolled by
+  // two with ping-pong registers (no register copies; on the last step the
+  // extra conversion reads a stale stage and is unused).
   static_assert(C::NSTAGE == 3, "two steps of prefetch");
   const int nk = (int)(K / C::BK);
-  uint32_t nsa[2], nsb[2] = {0u, 0u};
+  uint32_t sa[2], sb[2] = {0u, 0u};
   issue(0, 0);
 #pragma unroll
-  for (int j = 0; j < 2; j++) nsa[j] = scale_raw(j, 0);
+  for (int j = 0; j < 2; j++) sa[j] = scale_raw(j, 0);
   if (nk > 1) {
     issue(1, C::BK);
 #pragma unroll
-    for (int j = 0; j < 2; j++) nsb[j] = scale_raw(j, C::BK);
+    for (int j = 0; j < 2; j++) sb[j] = scale_raw(j, C::BK);
   }
+  wait_vm<0>();
+  tile_barrier();
 
-  int stage = 0;
-  auto step = [&](int kt, uint32_t (&ns)[2]) {
-    // group kt has landed for this wave (group kt + 1 may still be in flight);
-    // the barrier makes every wave's visible and guarantees that the stage the
-    // next group overwrites (read in step kt - 1) is no longer being read
-    if (kt + 1 < nk) wait_vm<C::VM_STEP>();
-    else wait_vm<0>();
-    tile_barrier();
-    float cs[2];
-#pragma unroll
-    for (int j = 0; j < 2; j++) cs[j] = scale_val(ns[j]);
-    if (kt + 2 < nk) {
-      issue(stage == 0 ? 2 : stage - 1, (int64_t)(kt + 2) * C::BK);
-#pragma unroll
-      for (int j = 0; j < 2; j++) ns[j] = scale_raw(j, (int64_t)(kt + 2) * C::BK);
-    }
-    const uint8_t* A = lds + stage * C::STAGE;
-    const uint8_t* B = A + C::A_TILE;
-    stage = stage == 2 ? 0 : stage + 1;
-    bf16x8_t bq[2][4];
+  // quarter q (k16 slice q) of a step's W fragments for both column subtiles
+  auto dequant_q = [&](const uint8_t* B, int q, const float (&cs)[2], bf16x8_t (&out)[4][2]) {
 #pragma unroll
     for (int j = 0; j < 2; j++) {
       const int br = wn * 64 + 32 * j + l32;
       const uint8_t* bp = B + br * C::wbytes;
       const int sw = bswz<LPR>(br);
       if constexpr (WTraits<WDT>::bits == 4) {
-        dequant16<WDT>(ld16(bp + 16 * (h ^ sw)), cs[j], bq[j]);
+        const uint32_t wd = *reinterpret_cast<const uint32_t*>(bp + 16 * (h ^ sw) + 4 * q);
+        uint32_t o[4];
+        if constexpr (WDT == W_INT4) dq_int4_word(wd, cs[j], o);
+        else dq_fp4_word(wd, cs[j], o);
+        out[q][j] = as_bf16x8(o[0], o[1], o[2], o[3]);
       } else {
-        dequant16<WDT>(ld16(bp + 16 * ((2 * h) ^ sw)), 1.0f, bq[j]);
-        dequant16<WDT>(ld16(bp + 16 * ((2 * h + 1) ^ sw)), 1.0f, bq[j] + 2);
+        const uint2 v = *reinterpret_cast<const uint2*>(bp + 16 * ((2 * h + (q >> 1)) ^ sw) + 8 * (q & 1));
+        out[q][j] = as_bf16x8(dq_fp8_pair<false>(v.x), dq_fp8_pair<true>(v.x), dq_fp8_pair<false>(v.y),
+                              dq_fp8_pair<true>(v.y));
       }
     }
+  };
+  bf16x8_t ba[4][2], bb[4][2];
+  {
+    float c0[2];
+#pragma unroll
+    for (int j = 0; j < 2; j++) c0[j] = scale_val(sa[j]);
+#pragma unroll
+    for (int q = 0; q < 4; q++) dequant_q(lds + C::A_TILE, q, c0, ba);
+  }
+
+  int stage = 0;
+  auto step = [&](int kt, bf16x8_t (&bcur)[4][2], bf16x8_t (&bnext)[4][2], uint32_t (&snext)[2],
+                  uint32_t (&sload)[2]) {
+    const int st1 = stage == 2 ? 0 : stage + 1;
+    const int st2 = st1 == 2 ? 0 : st1 + 1;
+    float cn[2];
+#pragma unroll
+    for (int j = 0; j < 2; j++) cn[j] = scale_val(snext[j]);
+    if (kt + 2 < nk) {
+      issue(st2, (int64_t)(kt + 2) * C::BK);
+#pragma unroll
+      for (int j = 0; j < 2; j++) sload[j] = scale_raw(j, (int64_t)(kt + 2) * C::BK);
+    }
+    const uint8_t* A = lds + stage * C::STAGE;
+    const uint8_t* Bn = lds + st1 * C::STAGE + C::A_TILE;
 #pragma unroll
     for (int s4 = 0; s4 < 4; s4++) {
       bf16x8_t af[4];
@@ -391,16 +410,20 @@ __global__ __launch_bounds__(512) void k_gemm8(const uint16_t* __restrict__ x, i
         const int r = wm * 128 + 32 * i + l32;
         af[i] = as_bf16x8(ld16(A + r * 128 + (((4 * h + s4) ^ (r & 7)) << 4)));
       }
+      dequant_q(Bn, s4, cn, bnext);
 #pragma unroll
       for (int i = 0; i < 4; i++)
 #pragma unroll
         for (int j = 0; j < 2; j++)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bq[j][s4], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bcur[s4][j], acc[i][j], 0, 0, 0);
     }
+    wait_vm<0>();
+    tile_barrier();
+    stage = st1;
   };
   for (int kt = 0; kt < nk; kt += 2) {
-    step(kt, nsa);
-    if (kt + 1 < nk) step(kt + 1, nsb);
+    step(kt, ba, bb, sb, sa);
+    if (kt + 1 < nk) step(kt + 1, bb, ba, sa, sb);
   }
 
   // epilogue: C element r of a 32x32 tile sits at row 8*(r/4) + 4*h + r%4, col l32.
