@@ -23,6 +23,10 @@ formats   number-format algebra and decode tables (bias, max finite, min normal,
 e4m3      fp32 -> OCP E4M3 "fn", RNE + satfinite; per-block and per-row scaling
 e8m0      the exponent-first 0.75-threshold E8M0 shared-scale rule
 mxfp4     E2M1 element rounding and the MXFP4 block quantizer
+mx        MX block quantizers under five E8M0 rules (exponent-first with the
+          format's rounding increment, threshold 0.5, strict OCP, the old
+          reciprocal-multiply rule, the round-up division rule) for E2M1 and E4M3
+          elements
 int4      symmetric INT4 group quantizer with bf16 scales
 dequant   packed weights + scales -> bf16 operands
 gemm      fp64 reference matmul and the acceptance bound
