@@ -15,14 +15,15 @@ synchronisation; `value` is algorithmic bytes / time.
 The same JSON line carries the roofline of that kernel (HIP events over the
 timed region on the launch stream), the oracle timed on the host (`cpu_baseline`)
 and `secondary` measurements: decode at M = 4 and 16, W8A16, prefill MXFP4 at
-M = 8192 (TFLOP/s), the activation quantizers at 4096 x 7168, the MXFP4 weight
-quantizer, the W4A8 mixture-of-experts grouped GEMMs (gate/up and down, with
+M = 8192 (TFLOP/s), the activation quantizers at 4096 x 7168 (E4M3 per 128,
+MXFP4 per 16, MXFP8 per 32 under two E8M0 rules, and the share of blocks whose
+maximum clips under each rule), the MXFP4 weight quantizer, the W4A8 mixture-of-experts grouped GEMMs (gate/up and down, with
 routing, token quantization and prepack), a streaming copy and torch.matmul
 (hipBLASLt) at the prefill shape as secondary denominators.
 
 --only CASE runs a single case without the full summary (for rocprofv3):
 decode (the same graph-timed steps as the headline, prints one short JSON
-line), decode_w8, prefill, quant_e4m3, quant_mxfp4, wquant_mxfp4, copy,
+line), decode_w8, prefill, quant_e4m3, quant_mxfp4, quant_mxfp8, wquant_mxfp4, copy,
 moe_gate_up, moe_down.
 """
 from __future__ import annotations
@@ -186,38 +187,46 @@ class Prefill:
 
 
 class ActQuant:
-    """4096 x 7168 bf16 -> E4M3 per 1x128 (fp32 scales) or MXFP4 per 16 (E8M0)."""
+    """4096 x 7168 bf16 -> E4M3 per 1x128 (fp32 scales), MXFP4 per 16 (E8M0) or
+    MXFP8 (E4M3 elements, E8M0 per 32) under a chosen scale rule."""
 
-    def __init__(self, torch, W, kind):
+    def __init__(self, torch, W, kind, rule="round"):
         from synthetic import act_quant_inputs
-        self.torch, self.W, self.kind = torch, W, kind
+        self.torch, self.W, self.kind, self.rule = torch, W, kind, rule
         bits = act_quant_inputs(0)
         x = dev_bf16(torch, bits)
         rows, cols = bits.shape
         inb = rows * cols * 2
         if kind == "e4m3":
-            outb = rows * cols + rows * (cols // 128) * 4
+            shapes = ((rows, cols), torch.uint8), ((rows, cols // 128), torch.float32)
+        elif kind == "mxfp4":
+            shapes = ((rows, cols // 2), torch.uint8), ((rows, cols // 16), torch.uint8)
         else:
-            outb = rows * cols // 2 + rows * (cols // 16)
+            shapes = ((rows, cols), torch.uint8), ((rows, cols // 32), torch.uint8)
+        outb = sum(a * b * (4 if dt == torch.float32 else 1) for (a, b), dt in shapes)
         self.bytes = inb + outb
         ncopy = max(1, int(ROTATE_BYTES // self.bytes) + 1)
         self.xs = [x] + [x.clone() for _ in range(ncopy - 1)]
-        self.outs = []
-        for _ in range(ncopy):
-            if kind == "e4m3":
-                self.outs.append((torch.empty((rows, cols), dtype=torch.uint8, device="cuda"),
-                                  torch.empty((rows, cols // 128), dtype=torch.float32, device="cuda")))
-            else:
-                self.outs.append((torch.empty((rows, cols // 2), dtype=torch.uint8, device="cuda"),
-                                  torch.empty((rows, cols // 16), dtype=torch.uint8, device="cuda")))
+        self.outs = [tuple(torch.empty(sh, dtype=dt, device="cuda") for sh, dt in shapes) for _ in range(ncopy)]
 
     def launch(self, i):
         j = i % len(self.xs)
         c, s = self.outs[j]
         if self.kind == "e4m3":
             self.W.quantize_e4m3(self.xs[j], 128, codes=c, scales=s)
-        else:
+        elif self.kind == "mxfp4":
             self.W.quantize_mxfp4(self.xs[j], 16, codes=c, scales=s)
+        else:
+            self.W.quantize_mx(self.xs[j], 32, "e4m3", self.rule, codes=c, scales=s)
+
+
+def clip_share(torch, W, x, block, elem, rule):
+    """Share of blocks whose maximum lands above the element maximum (it then
+    saturates) under `rule`, from the GPU scales of one quantize_mx call."""
+    _, sc = W.quantize_mx(x, block, elem, rule)
+    amax = x.float().abs().view(x.shape[0], -1, block).amax(dim=2)
+    ratio = amax / torch.exp2(sc.float() - 127.0)
+    return round(float((ratio > (6.0 if elem == "e2m1" else 448.0)).float().mean()), 5)
 
 
 class WeightQuant:
@@ -336,6 +345,7 @@ def main():
         mk = {"decode_w8": lambda: Decode(torch, W, 1, "e4m3"),
               "prefill": lambda: Prefill(torch, W), "quant_e4m3": lambda: ActQuant(torch, W, "e4m3"),
               "quant_mxfp4": lambda: ActQuant(torch, W, "mxfp4"), "copy": lambda: Copy(torch),
+              "quant_mxfp8": lambda: ActQuant(torch, W, "mxfp8"),
               "wquant_mxfp4": lambda: WeightQuant(torch, W),
               "moe_gate_up": lambda: MoeW4A8(torch, W, "gate_up"), "moe_down": lambda: MoeW4A8(torch, W, "down")}[case]
         obj = mk()
@@ -395,14 +405,20 @@ def main():
     del pf, wb
     torch.cuda.empty_cache()
 
-    for kind in ("e4m3", "mxfp4"):
-        q = ActQuant(torch, W, kind)
+    for kind, rule in (("e4m3", None), ("mxfp4", None), ("mxfp8", "round"), ("mxfp8", "ceil_div")):
+        q = ActQuant(torch, W, kind, rule)
         g = graph_of(torch, [lambda i=i: q.launch(i) for i in range(40)])
         g.replay()
         t = time_graph(torch, g, 40)
-        secondary[f"act_quant_{kind}_4096x7168"] = {"GB/s": round(q.bytes / (t * 1e-3) / 1e9, 1),
-                                                    "us": round(t * 1e3, 2),
-                                                    "frac_hbm": round(q.bytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        label = f"act_quant_{kind}_4096x7168" + (f"_{rule}" if rule else "")
+        secondary[label] = {"GB/s": round(q.bytes / (t * 1e-3) / 1e9, 1), "us": round(t * 1e3, 2),
+                            "frac_hbm": round(q.bytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        if kind == "mxfp8" and rule == "round":
+            shares = {}
+            for elem, block in (("e2m1", 16), ("e2m1", 32), ("e4m3", 32)):
+                for r in W.MX_RULES:
+                    shares[f"{elem}_b{block}_{r}"] = clip_share(torch, W, q.xs[0], block, elem, r)
+            secondary["mx_rule_clip_share_4096x7168"] = shares
         del g, q
     wq_ = WeightQuant(torch, W)
     t = time_eager(torch, wq_.launch, 10)

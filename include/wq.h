@@ -104,6 +104,50 @@ wq_status quantize_e4m3(const void* x, int x_dtype, int64_t rows, int64_t cols,
 wq_status quantize_mxfp4(const void* x, int x_dtype, int64_t rows, int64_t cols,
                          int32_t block, uint8_t* codes, uint8_t* scales, void* stream);
 
+/* E8M0 scale rules of quantize_mx; vmax is the fp32 block maximum magnitude,
+ * m the element mantissa width (1 for E2M1, 3 for E4M3), off its top binade (2
+ * for E2M1, 8 for E4M3), emax its largest value (6 or 448).                  */
+typedef enum {
+  WQ_MX_ROUND = 0,      /* biased_exp(bits(vmax) + 2^(22-m)) - off, clamped at 0  */
+  WQ_MX_HALF = 1,       /* biased_exp(bits(vmax) + 2^22) - off, clamped at 0      */
+  WQ_MX_OCP = 2,        /* biased_exp(vmax) - off, clamped at 0                   */
+  WQ_MX_FLOOR_DIV = 3,  /* biased_exp(RN_f32(vmax * RN_f32(1/emax)))             */
+  WQ_MX_CEIL_DIV = 4    /* max(ceil(log2(RN_f32(vmax / emax))), -127) + 127       */
+} wq_mx_rule;
+
+/*
+ * quantize_mx -- fp32/bf16 -> MX block format (E2M1 or E4M3 element codes +
+ * E8M0 block scale) under a choice of scale rule.
+ *
+ * Rules: "Fix the E8M0 scale computation in the MXFP4 (W4A4) MOE CUTLASS
+ * kernel" (vLLM PR #43557): WQ_MX_ROUND is the rule of section "Fix:
+ * Exponent-First with 0.75-Threshold Rounding", with the increment of section
+ * "Origin: Matching the Quantization Toolchain" for an m-bit mantissa (2^21 for
+ * E2M1, 2^19 for E4M3); WQ_MX_OCP and WQ_MX_HALF are the strict OCP and
+ * 0.5-threshold rows of "Why This Helps Precision (Not Strict OCP MX)";
+ * WQ_MX_FLOOR_DIV is the old rule of "Root Cause" (the reciprocal is the
+ * correctly rounded fp32 one).  WQ_MX_CEIL_DIV is SGLang's quantizer in
+ * "Numerics: FP32 to INT4, and why bf16 won", section "MXFP4 and the
+ * block-scaled family" (the quotient rounded up to a power of two, exactly).
+ * The element formats are from the OCP MX list on that page (mxfp4,
+ * mxfp8_e4m3).  An all-zero block gets code 0 under every rule.
+ *
+ * Elements: v = x * 2^(127-c); E2M1: nearest E2M1 value, ties to even code,
+ * saturating at 6 (as quantize_mxfp4); E4M3: RNE, saturating at 448.
+ * WQ_MX_ROUND with WQ_E2M1X2 gives exactly the output of quantize_mxfp4.
+ *
+ * x       rows x cols, dtype x_dtype (WQ_F32 or WQ_BF16); cols % 32 == 0.
+ * block   16 or 32.
+ * elem    WQ_E2M1X2 (codes rows x cols/2 bytes, element 2j in the low nibble
+ *         of byte j) or WQ_E4M3 (codes rows x cols bytes).
+ * rule    a wq_mx_rule; anything else is WQ_EINVAL.
+ * scales  rows x cols/block E8M0 bytes (output).
+ * Blocks holding a non-finite value are outside the contract (unspecified
+ * codes and scale, no error).
+ */
+wq_status quantize_mx(const void* x, int x_dtype, int64_t rows, int64_t cols, int32_t block,
+                      int32_t elem, int32_t rule, uint8_t* codes, uint8_t* scales, void* stream);
+
 /*
  * quantize_int4 -- fp32/bf16 weights -> symmetric INT4 with bf16 group scales.
  *

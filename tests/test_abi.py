@@ -26,7 +26,7 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("quantize_e4m3", "quantize_mxfp4", "quantize_int4", "wq_dequant", "wq_gemm",
+    for n in ("quantize_e4m3", "quantize_mxfp4", "quantize_mx", "quantize_int4", "wq_dequant", "wq_gemm",
               "wq_gemm_workspace_size", "wq_status_string", "wq_moe_route", "wq_w4a8_prepack",
               "wq_w4a8_dequant", "wq_moe_gemm_w4a8"):
         assert n in names
@@ -72,6 +72,15 @@ def test_invalid_arguments_rejected_before_launch(lib):
     g.restype = ctypes.c_int
     assert g(p, 0, _i64(4), _i64(64), 8, p, p, None) == 3
     assert g(p, 0, _i64(4), _i64(48), 32, p, p, None) == 1
+    m = lib.quantize_mx
+    m.restype = ctypes.c_int
+    assert m(p, 0, _i64(4), _i64(64), 32, 4, 0, p, p, None) == 3          # E8M0 is no element format
+    assert m(p, 0, _i64(4), _i64(64), 32, 2, 5, p, p, None) == 1          # unknown rule
+    assert m(p, 0, _i64(4), _i64(64), 32, 3, -1, p, p, None) == 1
+    assert m(p, 0, _i64(4), _i64(64), 64, 2, 0, p, p, None) == 3          # block
+    assert m(p, 0, _i64(4), _i64(48), 16, 2, 0, p, p, None) == 1          # cols % 32
+    assert m(p, 0, _i64(4), _i64(64), 32, 2, 0, p, None, None) == 1       # scales NULL
+    assert m(q, 0, _i64(4), _i64(64), 32, 3, 4, p, p, None) == 2          # misaligned
     h = lib.quantize_int4
     h.restype = ctypes.c_int
     assert h(p, 0, _i64(4), _i64(128), 96, p, p, None) == 3

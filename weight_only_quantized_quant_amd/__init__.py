@@ -21,6 +21,9 @@ LIB_PATH = os.path.join(_HERE, "libwq.so")
 # dtype enum of the C ABI
 WQ_F32, WQ_BF16, WQ_E4M3, WQ_E2M1X2, WQ_E8M0, WQ_INT4X8 = range(6)
 WQ_OK, WQ_EINVAL, WQ_EALIGN, WQ_EUNSUPPORTED, WQ_EHIP = range(5)
+# E8M0 scale rules of quantize_mx (wq_mx_rule)
+MX_RULES = {"round": 0, "half": 1, "ocp": 2, "floor_div": 3, "ceil_div": 4}
+MX_ELEMS = {"e2m1": WQ_E2M1X2, "e4m3": WQ_E4M3}
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -34,6 +37,7 @@ _SIGS = {
     "wq_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "quantize_e4m3": ([_vp, ctypes.c_int, _i64, _i64, _i32, _vp, _vp, _vp], ctypes.c_int),
     "quantize_mxfp4": ([_vp, ctypes.c_int, _i64, _i64, _i32, _vp, _vp, _vp], ctypes.c_int),
+    "quantize_mx": ([_vp, ctypes.c_int, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp], ctypes.c_int),
     "quantize_int4": ([_vp, ctypes.c_int, _i64, _i64, _i32, _vp, _vp, _vp], ctypes.c_int),
     "wq_dequant": ([_vp, ctypes.c_int, _vp, ctypes.c_int, _i32, _i64, _i64, _vp, _vp], ctypes.c_int),
     "wq_gemm": ([_vp, _i64, _i64, _i64, _vp, ctypes.c_int, _vp, ctypes.c_int, _i32, _vp, _vp, _sz, _vp],
@@ -124,6 +128,25 @@ def quantize_mxfp4(x: torch.Tensor, block: int = 32, codes=None, scales=None):
     scales = _out(scales, (rows, cols // block), torch.uint8, x.device, "scales")
     _check(lib.quantize_mxfp4(x.data_ptr(), _x_dtype(x), rows, cols, block, codes.data_ptr(), scales.data_ptr(),
                               _stream()), "quantize_mxfp4")
+    return codes, scales
+
+
+def quantize_mx(x: torch.Tensor, block: int = 32, elem: str = "e4m3", rule: str = "round", codes=None,
+                scales=None):
+    """x: 2-D fp32/bf16 -> (codes uint8, E8M0 scales uint8 [rows, cols/block]).
+    elem "e2m1": codes [rows, cols/2], two per byte; "e4m3": codes [rows, cols].
+    rule: one of MX_RULES."""
+    _dev(x, "x")
+    rows, cols = x.shape
+    if elem not in MX_ELEMS or rule not in MX_RULES:
+        raise ValueError(f"elem must be one of {sorted(MX_ELEMS)} and rule one of {sorted(MX_RULES)}")
+    if block not in (16, 32) or cols % 32:
+        raise ValueError("block must be 16 or 32 and cols a multiple of 32")
+    width = cols // 2 if elem == "e2m1" else cols
+    codes = _out(codes, (rows, width), torch.uint8, x.device, "codes")
+    scales = _out(scales, (rows, cols // block), torch.uint8, x.device, "scales")
+    _check(lib.quantize_mx(x.data_ptr(), _x_dtype(x), rows, cols, block, MX_ELEMS[elem], MX_RULES[rule],
+                           codes.data_ptr(), scales.data_ptr(), _stream()), "quantize_mx")
     return codes, scales
 
 

@@ -1,4 +1,5 @@
-// Block-scaled quantizers (fp32/bf16 -> E4M3, MXFP4, INT4) and the dequantizer
+// Block-scaled quantizers (fp32/bf16 -> E4M3, MXFP4, MX with a choice of scale
+// rule and E2M1 or E4M3 elements, INT4) and the dequantizer
 // entry point, for gfx950.  Memory-bound: every thread moves 16-byte vectors;
 // block maxima are reduced across the lanes that share a block with xor
 // shuffles.
@@ -151,6 +152,78 @@ __global__ __launch_bounds__(kThreads) void k_mxfp4(const void* __restrict__ x, 
 }
 
 // ---------------------------------------------------------------------------
+// MX block quantizer with a selectable E8M0 rule and E2M1 or E4M3 elements.
+// Same thread layout as k_mxfp4: 16 elements per thread, lane pairs for block 32.
+// ---------------------------------------------------------------------------
+
+// E8M0 code of a block maximum.  Exponent rules add an increment to the fp32
+// pattern (the sum stays below 2^31 for finite input), take the biased
+// exponent and subtract the element format's top binade (2 for E2M1, 8 for
+// E4M3).  The division rules take the exponent of an fp32 quotient by the
+// element maximum: floor via a multiply by its fp32 reciprocal, ceil via a
+// correctly rounded division, rounded up to a power of two exactly (a nonzero
+// fraction adds one; a subnormal quotient above 2^-127 gives 1).
+template <bool E4M3>
+__device__ __forceinline__ uint32_t mx_code(float vmax, int rule) {
+  constexpr uint32_t kOff = E4M3 ? 8u : 2u;
+  const uint32_t bits = __float_as_uint(vmax) & 0x7FFFFFFFu;
+  const float a = __uint_as_float(bits);
+  if (rule == WQ_MX_FLOOR_DIV) return __float_as_uint(a * (E4M3 ? 1.0f / 448.0f : 1.0f / 6.0f)) >> 23;
+  if (rule == WQ_MX_CEIL_DIV) {
+    const uint32_t qb = __float_as_uint(a / (E4M3 ? 448.0f : 6.0f));
+    const uint32_t be = qb >> 23;
+    return be ? be + ((qb & 0x7FFFFFu) != 0u) : (uint32_t)(qb > 0x400000u);
+  }
+  const uint32_t inc = rule == WQ_MX_ROUND ? (E4M3 ? 1u << 19 : 1u << 21) : (rule == WQ_MX_HALF ? 1u << 22 : 0u);
+  const uint32_t be = (bits + inc) >> 23;
+  return be > kOff ? be - kOff : 0u;
+}
+
+template <bool BF16, bool E4M3>
+__global__ __launch_bounds__(kThreads) void k_mx(const void* __restrict__ x, int64_t nchunks, int block, int rule,
+                                                uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int64_t t0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const bool valid = t0 < nchunks;
+  const int64_t t = valid ? t0 : nchunks - 1;
+  float v[16];
+  load8<BF16>(x, t * 16, v);
+  load8<BF16>(x, t * 16 + 8, v + 8);
+  float m = __builtin_fmaxf(absmax8(v), absmax8(v + 8));
+  if (block == 32) m = __builtin_fmaxf(m, __shfl_xor(m, 1, 64));
+  const uint32_t code = mx_code<E4M3>(m, rule);
+  if constexpr (E4M3) {
+    // x * 2^(127 - c) is exact (or underflows far below the E4M3 grid); the
+    // clamp saturates what lies above 448 before the RNE conversion
+    const int sh = 127 - (int)code;
+    float q[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) q[i] = clamp448(__builtin_ldexpf(v[i], sh));
+    u32x4_t out;
+#pragma unroll
+    for (int d = 0; d < 4; d++) {
+      uint32_t r = e4m3_pack2<false>(q[4 * d], q[4 * d + 1], 0u);
+      out[d] = e4m3_pack2<true>(q[4 * d + 2], q[4 * d + 3], r);
+    }
+    if (valid) *reinterpret_cast<u32x4_t*>(codes + t * 16) = out;
+  } else {
+    const float sc = e8m0_as_scale(code);
+    uint32_t w0 = e2m1_pack2<0>(0u, v[0], v[1], sc);
+    w0 = e2m1_pack2<1>(w0, v[2], v[3], sc);
+    w0 = e2m1_pack2<2>(w0, v[4], v[5], sc);
+    w0 = e2m1_pack2<3>(w0, v[6], v[7], sc);
+    uint32_t w1 = e2m1_pack2<0>(0u, v[8], v[9], sc);
+    w1 = e2m1_pack2<1>(w1, v[10], v[11], sc);
+    w1 = e2m1_pack2<2>(w1, v[12], v[13], sc);
+    w1 = e2m1_pack2<3>(w1, v[14], v[15], sc);
+    if (valid) *reinterpret_cast<u32x2_t*>(codes + t * 8) = u32x2_t{w0, w1};
+  }
+  if (valid) {
+    if (block == 16) scales[t] = (uint8_t)code;
+    else if ((threadIdx.x & 1) == 0) scales[t >> 1] = (uint8_t)code;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // INT4 symmetric groups: 16 elements per thread, group/16 lanes per group.
 // ---------------------------------------------------------------------------
 template <bool BF16>
@@ -267,6 +340,29 @@ wq_status quantize_mxfp4(const void* x, int x_dtype, int64_t rows, int64_t cols,
   const int64_t nch = rows * cols / 16;
   if (x_dtype == WQ_BF16) k_mxfp4<true><<<grid_for(nch), kThreads, 0, s>>>(x, nch, block, codes, scales);
   else k_mxfp4<false><<<grid_for(nch), kThreads, 0, s>>>(x, nch, block, codes, scales);
+  return wq_launch_status();
+}
+
+wq_status quantize_mx(const void* x, int x_dtype, int64_t rows, int64_t cols, int32_t block, int32_t elem,
+                      int32_t rule, uint8_t* codes, uint8_t* scales, void* stream) {
+  if (!x || !codes || !scales || rows <= 0 || cols <= 0) return WQ_EINVAL;
+  if (x_dtype != WQ_F32 && x_dtype != WQ_BF16) return WQ_EUNSUPPORTED;
+  if (elem != WQ_E2M1X2 && elem != WQ_E4M3) return WQ_EUNSUPPORTED;
+  if (rule < WQ_MX_ROUND || rule > WQ_MX_CEIL_DIV) return WQ_EINVAL;
+  if (block != 16 && block != 32) return WQ_EUNSUPPORTED;
+  if (cols % 32 || !wq_numel_ok(rows, cols)) return WQ_EINVAL;
+  if (!wq_aligned(x) || !wq_aligned(codes) || !wq_aligned(scales)) return WQ_EALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t nch = rows * cols / 16;
+  const unsigned g = grid_for(nch);
+  const bool bf = x_dtype == WQ_BF16;
+  if (elem == WQ_E4M3) {
+    if (bf) k_mx<true, true><<<g, kThreads, 0, s>>>(x, nch, block, rule, codes, scales);
+    else k_mx<false, true><<<g, kThreads, 0, s>>>(x, nch, block, rule, codes, scales);
+  } else {
+    if (bf) k_mx<true, false><<<g, kThreads, 0, s>>>(x, nch, block, rule, codes, scales);
+    else k_mx<false, false><<<g, kThreads, 0, s>>>(x, nch, block, rule, codes, scales);
+  }
   return wq_launch_status();
 }
 
