@@ -27,6 +27,7 @@ mx        MX block quantizers under five E8M0 rules (exponent-first with the
           format's rounding increment, threshold 0.5, strict OCP, the old
           reciprocal-multiply rule, the round-up division rule) for E2M1 and E4M3
           elements
+nvfp4     NVFP4: E2M1 blocks of 16 with an E4M3 scale and a per-tensor fp32 scale
 int4      symmetric INT4 group quantizer with bf16 scales
 dequant   packed weights + scales -> bf16 operands
 gemm      fp64 reference matmul and the acceptance bound
