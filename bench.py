@@ -14,16 +14,17 @@ synchronisation; `value` is algorithmic bytes / time.
 
 The same JSON line carries the roofline of that kernel (HIP events over the
 timed region on the launch stream), the oracle timed on the host (`cpu_baseline`)
-and `secondary` measurements: decode at M = 4 and 16, W8A16, prefill MXFP4 at
-M = 8192 (TFLOP/s), the activation quantizers at 4096 x 7168 (E4M3 per 128,
-MXFP4 per 16, MXFP8 per 32 under two E8M0 rules, and the share of blocks whose
-maximum clips under each rule), the MXFP4 weight quantizer, the W4A8 mixture-of-experts grouped GEMMs (gate/up and down, with
-routing, token quantization and prepack), a streaming copy and torch.matmul
-(hipBLASLt) at the prefill shape as secondary denominators.
+and `secondary` measurements: decode at M = 4 and 16, W8A16, NVFP4 decode at
+M = 1 and 16, prefill MXFP4 and NVFP4 at M = 8192 (TFLOP/s), the activation
+quantizers at 4096 x 7168 (E4M3 per 128, MXFP4 per 16, MXFP8 per 32 under two
+E8M0 rules, and the share of blocks whose maximum clips under each rule), the
+MXFP4 weight quantizer, the W4A8 mixture-of-experts grouped GEMMs (gate/up and
+down, with routing, token quantization and prepack), a streaming copy and
+torch.matmul (hipBLASLt) at the prefill shape as secondary denominators.
 
 --only CASE runs a single case without the full summary (for rocprofv3):
 decode (the same graph-timed steps as the headline, prints one short JSON
-line), decode_w8, prefill, quant_e4m3, quant_mxfp4, quant_mxfp8, wquant_mxfp4, copy,
+line), decode_w8, decode_nvfp4, prefill, prefill_nvfp4, quant_e4m3, quant_mxfp4, quant_mxfp8, wquant_mxfp4, copy,
 moe_gate_up, moe_down.
 """
 from __future__ import annotations
@@ -134,8 +135,14 @@ def stored_traffic(case, bytes_per_launch):
 # workloads
 # ---------------------------------------------------------------------------
 
+def nvfp4_tensor_scale(torch, w):
+    """Per-tensor scale that maps the tensor's maximum to 6 * 448."""
+    return float(w.abs().max().item()) / (6.0 * 448.0)
+
+
 class Decode:
-    """x[M, 4096] . dequant(W[14336, 4096])^T, INT4 g128 or E4M3 per-channel."""
+    """x[M, 4096] . dequant(W[14336, 4096])^T, INT4 g128, E4M3 per-channel or
+    NVFP4 (E4M3 scale per 16, per-tensor fp32 scale)."""
 
     def __init__(self, torch, W, M, kind="int4", K=4096, N=14336):
         from synthetic import decode_inputs
@@ -143,11 +150,18 @@ class Decode:
         xbits, Wf = decode_inputs(M, seed=0)
         self.x = dev_bf16(torch, xbits)
         wdev = torch.from_numpy(Wf).cuda()
+        self.alpha = 1.0
         if kind == "int4":
             packed, sb = W.quantize_int4(wdev, 128)
             self.wbytes = packed.numel() * 4 + sb.numel() * 2
             base = (packed, sb)
             self.meta = (W.WQ_INT4X8, W.WQ_BF16, 128)
+        elif kind == "nvfp4":
+            self.alpha = nvfp4_tensor_scale(torch, wdev)
+            codes, sc = W.quantize_nvfp4(wdev, self.alpha)
+            self.wbytes = codes.numel() + sc.numel()
+            base = (codes, sc)
+            self.meta = (W.WQ_E2M1X2, W.WQ_E4M3, 16)
         else:
             codes, sc = W.quantize_e4m3(wdev, -1)
             sc = sc.reshape(-1).contiguous()
@@ -164,26 +178,35 @@ class Decode:
     def launch(self, i):
         wq, sc = self.copies[i % len(self.copies)]
         wdt, sdt, grp = self.meta
-        self.W.wq_gemm(self.x, wq, wdt, sc, sdt, grp, self.N, y=self.y)
+        self.W.wq_gemm(self.x, wq, wdt, sc, sdt, grp, self.N, y=self.y, alpha=self.alpha)
 
 
 class Prefill:
-    """x[8192, 4096] . dequant(W_mxfp4[14336, 4096])^T."""
+    """x[8192, 4096] . dequant(W[14336, 4096])^T with MXFP4 (E8M0 per 32) or
+    NVFP4 (E4M3 per 16 and a per-tensor scale) weights."""
 
-    def __init__(self, torch, W, M=8192, K=4096, N=14336):
+    def __init__(self, torch, W, M=8192, K=4096, N=14336, kind="mxfp4"):
         from synthetic import prefill_inputs
-        self.torch, self.W, self.M, self.K, self.N = torch, W, M, K, N
+        self.torch, self.W, self.M, self.K, self.N, self.kind = torch, W, M, K, N, kind
         xbits, Wf = prefill_inputs(0, M=M, K=K, N=N)
         self.x = dev_bf16(torch, xbits)
         wdev = torch.from_numpy(Wf).cuda()
-        self.codes, self.sc = W.quantize_mxfp4(wdev, 32)
+        if kind == "nvfp4":
+            self.alpha = nvfp4_tensor_scale(torch, wdev)
+            self.codes, self.sc = W.quantize_nvfp4(wdev, self.alpha)
+            self.meta = (W.WQ_E2M1X2, W.WQ_E4M3, 16)
+        else:
+            self.alpha = 1.0
+            self.codes, self.sc = W.quantize_mxfp4(wdev, 32)
+            self.meta = (W.WQ_E2M1X2, W.WQ_E8M0, 32)
         del wdev
         self.y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
         self.flops = 2.0 * M * N * K
         self.bytes = self.codes.numel() + self.sc.numel() + M * K * 2 + M * N * 2
 
     def launch(self, i):
-        self.W.wq_gemm(self.x, self.codes, self.W.WQ_E2M1X2, self.sc, self.W.WQ_E8M0, 32, self.N, y=self.y)
+        wdt, sdt, grp = self.meta
+        self.W.wq_gemm(self.x, self.codes, wdt, self.sc, sdt, grp, self.N, y=self.y, alpha=self.alpha)
 
 
 class ActQuant:
@@ -342,14 +365,15 @@ def main():
     K, Wm = args.steps, args.warmup
     if args.only and args.only != "decode":
         case = args.only
-        mk = {"decode_w8": lambda: Decode(torch, W, 1, "e4m3"),
+        mk = {"decode_w8": lambda: Decode(torch, W, 1, "e4m3"), "decode_nvfp4": lambda: Decode(torch, W, 1, "nvfp4"),
+              "prefill_nvfp4": lambda: Prefill(torch, W, kind="nvfp4"),
               "prefill": lambda: Prefill(torch, W), "quant_e4m3": lambda: ActQuant(torch, W, "e4m3"),
               "quant_mxfp4": lambda: ActQuant(torch, W, "mxfp4"), "copy": lambda: Copy(torch),
               "quant_mxfp8": lambda: ActQuant(torch, W, "mxfp8"),
               "wquant_mxfp4": lambda: WeightQuant(torch, W),
               "moe_gate_up": lambda: MoeW4A8(torch, W, "gate_up"), "moe_down": lambda: MoeW4A8(torch, W, "down")}[case]
         obj = mk()
-        reps = args.reps or (10 if case in ("prefill", "moe_gate_up", "moe_down") else 100)
+        reps = args.reps or (10 if case in ("prefill", "prefill_nvfp4", "moe_gate_up", "moe_down") else 100)
         for i in range(reps):
             obj.launch(i)
         torch.cuda.synchronize()
@@ -390,6 +414,8 @@ def main():
     add_decode("decode_w4a16_m4", 4, "int4")
     add_decode("decode_w4a16_m16", 16, "int4")
     add_decode("decode_w8a16_m1", 1, "e4m3")
+    add_decode("decode_nvfp4_m1", 1, "nvfp4")
+    add_decode("decode_nvfp4_m16", 16, "nvfp4")
     torch.cuda.empty_cache()
 
     pf = Prefill(torch, W)
@@ -403,6 +429,12 @@ def main():
     secondary["torch_matmul_bf16_8192x14336x4096"] = {"TFLOP/s": round(pf.flops / (t2 * 1e-3) / 1e12, 1),
                                                       "ms": round(t2, 3)}
     del pf, wb
+    pf = Prefill(torch, W, kind="nvfp4")
+    t = time_eager(torch, pf.launch, 10)
+    tf = pf.flops / (t * 1e-3) / 1e12
+    secondary["prefill_nvfp4_m8192"] = {"TFLOP/s": round(tf, 1), "frac_bf16_mfma": round(tf / BF16_PEAK_TFLOPS, 4),
+                                        "ms": round(t, 3)}
+    del pf
     torch.cuda.empty_cache()
 
     for kind, rule in (("e4m3", None), ("mxfp4", None), ("mxfp8", "round"), ("mxfp8", "ceil_div")):

@@ -149,6 +149,32 @@ wq_status quantize_mx(const void* x, int x_dtype, int64_t rows, int64_t cols, in
                       int32_t elem, int32_t rule, uint8_t* codes, uint8_t* scales, void* stream);
 
 /*
+ * quantize_nvfp4 -- fp32/bf16 -> NVFP4 (E2M1 codes, one E4M3 scale per 16).
+ *
+ * "Numerics: FP32 to INT4, and why bf16 won", section "MXFP4 and the
+ * block-scaled family" (NVFP4: blocks of 16, the scale stored as E4M3, so it
+ * has mantissa bits and can sit between powers of two); "Your 3090 Isn't
+ * Missing Anything for FP8/NVFP4 Weight-Only Inference", section 2.1 (the
+ * block and its E4M3 scale decode to bf16 for a bf16 multiply); and the review
+ * note on vLLM PR #43557 (divide the elements by the dequantized scale).
+ * Per 1 x 16 block, with g = tensor_scale:
+ *   s8 = e4m3(RN_f32(RN_f32(amax / 6) / g)), RNE, saturating at 448;
+ *   d = RN_f32(e4m3_value(s8) * g);
+ *   code = e2m1(RN_f32(x / d)) (nearest, ties to even code, saturating at 6),
+ *   a zero of x's sign when d == 0.
+ * Dequantized value: g * e4m3_value(s8) * e2m1_value(code).  The per-tensor
+ * scale is not given on the pages; g = 1 is their description.
+ *
+ * x             rows x cols, dtype x_dtype (WQ_F32 or WQ_BF16); cols % 16 == 0.
+ * tensor_scale  finite and > 0 (WQ_EINVAL otherwise).
+ * codes         rows x cols/2 bytes (output), element 2j in the low nibble of byte j.
+ * scales        rows x cols/16 E4M3 bytes (output).
+ * Blocks holding a non-finite value are outside the contract.
+ */
+wq_status quantize_nvfp4(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                         float tensor_scale, uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
  * quantize_int4 -- fp32/bf16 weights -> symmetric INT4 with bf16 group scales.
  *
  * Follows "Numerics: FP32 to INT4, and why bf16 won" (x = s * (q - z), z = 0;
@@ -175,6 +201,10 @@ wq_status quantize_int4(const void* w, int w_dtype, int64_t rows, int64_t cols,
  *       rounding of the exact product.
  *   w_dtype WQ_E2M1X2 + s_dtype WQ_E8M0  (group 16/32): bf16(v * 2^(c-127)),
  *       exact; scale code 255 (E8M0 NaN) is outside the contract.
+ *   w_dtype WQ_E2M1X2 + s_dtype WQ_E4M3  (group 16, NVFP4): v * e4m3 value,
+ *       exact (every such product is a bf16 number); the per-tensor scale is
+ *       not applied (it is wq_gemm's alpha).  NaN scale codes are outside the
+ *       contract.
  *   w_dtype WQ_E4M3  (s_dtype WQ_F32, scales may be NULL; group ignored):
  *       bf16(v), exact; the per-channel scale is NOT applied (it multiplies the
  *       fp32 accumulator).  NaN codes give a NaN of unspecified sign.
@@ -195,9 +225,15 @@ wq_status wq_dequant(const void* wq, int w_dtype, const void* w_scales, int s_dt
  *
  * Weight/scale pairs:
  *   WQ_INT4X8 + WQ_BF16  group in {32, 64, 128}
- *   WQ_E2M1X2 + WQ_E8M0  group 32
+ *   WQ_E2M1X2 + WQ_E8M0  group 32 (MXFP4)
+ *   WQ_E2M1X2 + WQ_E4M3  group 16 (NVFP4; the operand is the exact product of
+ *                         the E2M1 and E4M3 values)
  *   WQ_E4M3   + WQ_F32   group == K (one fp32 scale per output channel, applied
  *                         to the fp32 accumulator before the bf16 rounding)
+ * alpha   an fp32 factor on the accumulator before the bf16 rounding (the
+ *         per-tensor scale of NVFP4; 1 otherwise).  Non-finite: WQ_EINVAL.
+ *         y = bf16(acc * RN(chan * alpha)) for WQ_E4M3 weights,
+ *         y = bf16(acc * alpha) for the others.
  * M >= 1, N >= 1, K % 128 == 0.  M <= 16 runs the split-K decode kernel,
  * larger M the MFMA prefill kernel.
  * workspace / ws_bytes: reserved; the current kernels need none
@@ -207,8 +243,8 @@ wq_status wq_dequant(const void* wq, int w_dtype, const void* w_scales, int s_dt
  */
 wq_status wq_gemm(const void* x_bf16, int64_t M, int64_t N, int64_t K,
                   const void* wq, int w_dtype, const void* w_scales, int s_dtype,
-                  int32_t group, void* y_bf16, void* workspace, size_t ws_bytes,
-                  void* stream);
+                  int32_t group, float alpha, void* y_bf16, void* workspace,
+                  size_t ws_bytes, void* stream);
 
 /* Bytes of workspace wq_gemm needs for this problem (currently always 0). */
 size_t wq_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int w_dtype, int32_t group);

@@ -46,7 +46,7 @@ def block_scale(amax_f32, g: float = 1.0):
     a = np.asarray(amax_f32, dtype=np.float32)
     if not np.isfinite(a).all():
         raise ValueError("non-finite block maximum")
-    with np.errstate(under="ignore"):
+    with np.errstate(under="ignore", over="ignore"):      # fp32 overflow saturates the scale
         s = ((a / np.float32(6.0)).astype(np.float32) / g32).astype(np.float32)
         s8 = e4m3_from_f32(s)
         d = (e4m3_decode(s8).astype(np.float32) * g32).astype(np.float32)
@@ -63,7 +63,7 @@ def quantize_nvfp4(x, g: float = 1.0):
     s8, d = block_scale(block_absmax(x32, BLOCK), g)
     xb = x32.reshape(rows, cols // BLOCK, BLOCK)
     dd = np.broadcast_to(d[:, :, None], xb.shape)
-    with np.errstate(divide="ignore", invalid="ignore", under="ignore"):
+    with np.errstate(divide="ignore", invalid="ignore", under="ignore", over="ignore"):
         v = np.where(dd > 0, (xb / np.where(dd > 0, dd, np.float32(1))).astype(np.float32), np.float32(0))
     sign = (f32_bits(xb) >> 31).astype(np.uint8)
     codes = e2m1_from_f64(v.astype(np.float64), sign).reshape(rows, cols)

@@ -26,7 +26,7 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("quantize_e4m3", "quantize_mxfp4", "quantize_mx", "quantize_int4", "wq_dequant", "wq_gemm",
+    for n in ("quantize_e4m3", "quantize_mxfp4", "quantize_mx", "quantize_nvfp4", "quantize_int4", "wq_dequant", "wq_gemm",
               "wq_gemm_workspace_size", "wq_status_string", "wq_moe_route", "wq_w4a8_prepack",
               "wq_w4a8_dequant", "wq_moe_gemm_w4a8"):
         assert n in names
@@ -92,14 +92,26 @@ def test_invalid_arguments_rejected_before_launch(lib):
     assert d(p, 5, p, 1, 128, _i64(4), _i64(100), p, None) == 1
     gm = lib.wq_gemm
     gm.restype = ctypes.c_int
-    args = lambda M, N, K, wdt, sdt, grp, x=p: (x, _i64(M), _i64(N), _i64(K), p, wdt, p, sdt, grp, p, None,
-                                               ctypes.c_size_t(0), None)
+    args = lambda M, N, K, wdt, sdt, grp, x=p, a=1.0: (x, _i64(M), _i64(N), _i64(K), p, wdt, p, sdt, grp,
+                                                      ctypes.c_float(a), p, None, ctypes.c_size_t(0), None)
     assert gm(*args(1, 16, 100, 5, 1, 128)) == 1                        # K % 128
     assert gm(*args(0, 16, 128, 5, 1, 128)) == 1
     assert gm(*args(1, 16, 128, 5, 1, 96)) == 3                         # bad group
     assert gm(*args(1, 16, 128, 3, 1, 32)) == 3                         # fp4 needs E8M0
     assert gm(*args(1, 16, 256, 2, 0, 128)) == 3                        # e4m3 needs group == K
     assert gm(*args(1, 16, 128, 5, 1, 128, x=q)) == 2
+    assert gm(*args(1, 16, 128, 3, 2, 32)) == 3                         # NVFP4 needs group 16
+    assert gm(*args(1, 16, 128, 3, 2, 16, a=float("nan"))) == 1         # alpha must be finite
+    assert gm(*args(1, 16, 128, 3, 2, 16, a=float("inf"))) == 1
+    nv = lib.quantize_nvfp4
+    nv.restype = ctypes.c_int
+    assert nv(p, 0, _i64(4), _i64(24), ctypes.c_float(1.0), p, p, None) == 1   # cols % 16
+    assert nv(p, 0, _i64(4), _i64(32), ctypes.c_float(0.0), p, p, None) == 1   # tensor scale > 0
+    assert nv(p, 0, _i64(4), _i64(32), ctypes.c_float(-1.0), p, p, None) == 1
+    assert nv(p, 0, _i64(4), _i64(32), ctypes.c_float(float("inf")), p, p, None) == 1
+    assert nv(p, 5, _i64(4), _i64(32), ctypes.c_float(1.0), p, p, None) == 3
+    assert nv(q, 0, _i64(4), _i64(32), ctypes.c_float(1.0), p, p, None) == 2
+    assert d(p, 3, p, 2, 32, _i64(4), _i64(128), p, None) == 3       # NVFP4 dequant needs group 16
     lib.wq_gemm_workspace_size.restype = ctypes.c_size_t
     assert lib.wq_gemm_workspace_size(_i64(1), _i64(16), _i64(128), 5, 128) == 0
 

@@ -76,6 +76,21 @@ def test_gemv_int4_small_groups(W, group):
     _check(W.wq_gemm(dev_bf16(xbits), *args, 300), xbits, wdeq, chan)
 
 
+@pytest.mark.parametrize("group", [32, 64])
+@pytest.mark.parametrize("M", [1, 4])
+def test_gemv_int4_small_groups_long_k(W, group, M):
+    # K = 8192 with group 32: each row of a wave's slice holds 128 bytes of
+    # scales, which take two staging loads per wave
+    K, N = 8192, 272
+    g = np.random.default_rng(group + 10 * M)
+    Wf = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
+    Wf[g.choice(N, 20, replace=False)] *= 8                      # rows with their own scales
+    xbits = to_bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    args, wdeq, chan = _prep(W, "int4", Wf, group)
+    banner("gemv int4 group", group, "M", M, "K", K)
+    _check(W.wq_gemm(dev_bf16(xbits), *args, N), xbits, wdeq, chan)
+
+
 def test_gemv_mxfp4_small_config(W):
     xbits, Wf = mxfp4_gemv_inputs(0)
     args, wdeq, chan = _prep(W, "mxfp4", Wf)

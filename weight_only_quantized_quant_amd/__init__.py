@@ -37,11 +37,12 @@ _SIGS = {
     "wq_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "quantize_e4m3": ([_vp, ctypes.c_int, _i64, _i64, _i32, _vp, _vp, _vp], ctypes.c_int),
     "quantize_mxfp4": ([_vp, ctypes.c_int, _i64, _i64, _i32, _vp, _vp, _vp], ctypes.c_int),
+    "quantize_nvfp4": ([_vp, ctypes.c_int, _i64, _i64, ctypes.c_float, _vp, _vp, _vp], ctypes.c_int),
     "quantize_mx": ([_vp, ctypes.c_int, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp], ctypes.c_int),
     "quantize_int4": ([_vp, ctypes.c_int, _i64, _i64, _i32, _vp, _vp, _vp], ctypes.c_int),
     "wq_dequant": ([_vp, ctypes.c_int, _vp, ctypes.c_int, _i32, _i64, _i64, _vp, _vp], ctypes.c_int),
-    "wq_gemm": ([_vp, _i64, _i64, _i64, _vp, ctypes.c_int, _vp, ctypes.c_int, _i32, _vp, _vp, _sz, _vp],
-                ctypes.c_int),
+    "wq_gemm": ([_vp, _i64, _i64, _i64, _vp, ctypes.c_int, _vp, ctypes.c_int, _i32, ctypes.c_float, _vp, _vp, _sz,
+                 _vp], ctypes.c_int),
     "wq_gemm_workspace_size": ([_i64, _i64, _i64, ctypes.c_int, _i32], _sz),
     "wq_moe_route": ([_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "wq_w4a8_prepack": ([_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp], ctypes.c_int),
@@ -131,6 +132,20 @@ def quantize_mxfp4(x: torch.Tensor, block: int = 32, codes=None, scales=None):
     return codes, scales
 
 
+def quantize_nvfp4(x: torch.Tensor, tensor_scale: float = 1.0, codes=None, scales=None):
+    """x: 2-D fp32/bf16 -> (codes uint8 [rows, cols/2], E4M3 scales uint8 [rows, cols/16]).
+    Dequantized value: tensor_scale * e4m3(scale) * e2m1(code)."""
+    _dev(x, "x")
+    rows, cols = x.shape
+    if cols % 16:
+        raise ValueError("cols must be a multiple of 16")
+    codes = _out(codes, (rows, cols // 2), torch.uint8, x.device, "codes")
+    scales = _out(scales, (rows, cols // 16), torch.uint8, x.device, "scales")
+    _check(lib.quantize_nvfp4(x.data_ptr(), _x_dtype(x), rows, cols, float(tensor_scale), codes.data_ptr(),
+                              scales.data_ptr(), _stream()), "quantize_nvfp4")
+    return codes, scales
+
+
 def quantize_mx(x: torch.Tensor, block: int = 32, elem: str = "e4m3", rule: str = "round", codes=None,
                 scales=None):
     """x: 2-D fp32/bf16 -> (codes uint8, E8M0 scales uint8 [rows, cols/block]).
@@ -180,7 +195,7 @@ def _check_scales(sc, s_dtype, N, K, group):
     if sc is None:
         return None
     _dev(sc, "w_scales")
-    per = {WQ_BF16: 2, WQ_E8M0: 1, WQ_F32: 4}[s_dtype]
+    per = {WQ_BF16: 2, WQ_E8M0: 1, WQ_E4M3: 1, WQ_F32: 4}[s_dtype]
     count = N if s_dtype == WQ_F32 else N * (K // group)
     if sc.numel() * sc.element_size() != count * per:
         raise ValueError("w_scales has the wrong size")
@@ -201,8 +216,8 @@ def wq_gemm_workspace_size(M: int, N: int, K: int, w_dtype: int, group: int) -> 
 
 
 def wq_gemm(x: torch.Tensor, wq: torch.Tensor, w_dtype: int, w_scales: torch.Tensor, s_dtype: int, group: int,
-            N: int, y=None, workspace=None):
-    """y[M, N] = x[M, K] . dequant(wq)^T in bf16 with fp32 accumulation."""
+            N: int, y=None, workspace=None, alpha: float = 1.0):
+    """y[M, N] = alpha * x[M, K] . dequant(wq)^T in bf16 with fp32 accumulation."""
     _dev(x, "x")
     if x.dtype != torch.bfloat16 or x.dim() != 2:
         raise ValueError("x must be a 2-D bfloat16 tensor")
@@ -214,8 +229,8 @@ def wq_gemm(x: torch.Tensor, wq: torch.Tensor, w_dtype: int, w_scales: torch.Ten
     if workspace is not None:
         _dev(workspace, "workspace")
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    _check(lib.wq_gemm(x.data_ptr(), M, N, K, wq.data_ptr(), w_dtype, sp, s_dtype, group, y.data_ptr(), ws_ptr,
-                       ws_bytes, _stream()), "wq_gemm")
+    _check(lib.wq_gemm(x.data_ptr(), M, N, K, wq.data_ptr(), w_dtype, sp, s_dtype, group, float(alpha), y.data_ptr(),
+                       ws_ptr, ws_bytes, _stream()), "wq_gemm")
     return y
 
 

@@ -54,6 +54,22 @@ __device__ __forceinline__ uint32_t dq_fp8_pair(uint32_t w) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// E2M1 word (8 codes) times an fp32 scale s -> 4 bf16 pairs.  The scaled
+// conversions read only the exponent of their scale operand, so the codes are
+// decoded unscaled (exact fp32), multiplied by s in fp32 and rounded once.  For
+// an E4M3-valued s every product is a bf16 number: the result is exact.
+template <int SEL>
+__device__ __forceinline__ uint32_t dq_fp4_pair_mul(uint32_t w, float s) {
+  const auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+  return pack_bf16x2(f[0] * s, f[1] * s);
+}
+__device__ __forceinline__ void dq_nv4_word(uint32_t w, float s, uint32_t out[4]) {
+  out[0] = dq_fp4_pair_mul<0>(w, s);
+  out[1] = dq_fp4_pair_mul<1>(w, s);
+  out[2] = dq_fp4_pair_mul<2>(w, s);
+  out[3] = dq_fp4_pair_mul<3>(w, s);
+}
+
 // fp32 scale operand whose exponent field is the E8M0 code c (c = 0 -> 0.0f,
 // which the scaled conversions read as 2^-127).
 __device__ __forceinline__ float e8m0_as_scale(uint32_t c) { return __uint_as_float(c << 23); }

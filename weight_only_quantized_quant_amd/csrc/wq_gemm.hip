@@ -20,12 +20,28 @@ using namespace wq;
 
 namespace {
 
-enum { W_INT4 = 0, W_FP4 = 1, W_FP8 = 2 };
+// W_NV4: E2M1 codes with an E4M3 scale per 16 elements (NVFP4).
+enum { W_INT4 = 0, W_FP4 = 1, W_FP8 = 2, W_NV4 = 3 };
 
 template <int WDT> struct WTraits;
 template <> struct WTraits<W_INT4> { static constexpr int bits = 4; };
 template <> struct WTraits<W_FP4> { static constexpr int bits = 4; };
 template <> struct WTraits<W_FP8> { static constexpr int bits = 8; };
+template <> struct WTraits<W_NV4> { static constexpr int bits = 4; };
+
+// log2 of the scale group along K (INT4: the caller's group) and bytes per scale
+template <int WDT>
+__host__ __device__ constexpr int gshift_of(int int4_shift) {
+  return WDT == W_INT4 ? int4_shift : WDT == W_NV4 ? 4 : 5;
+}
+template <int WDT> constexpr int scale_bytes() { return WDT == W_INT4 ? 2 : 1; }
+
+// Scale operand of one lane's 32-element chunk: one value, or for NVFP4 the
+// values of its two 16-element blocks.
+struct Sc2 { float lo, hi; };
+template <int WDT> struct ScaleT { using type = float; };
+template <> struct ScaleT<W_NV4> { using type = Sc2; };
+template <int WDT> using scale_t = typename ScaleT<WDT>::type;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   return __builtin_bit_cast(bf16x8_t, u32x4_t{a, b, c, d});
@@ -47,8 +63,15 @@ __device__ __forceinline__ float load_scale(const void* sc, int64_t row, int64_t
 // Convert one packed 16-byte weight chunk to bf16 MFMA operands.
 // 4-bit: 32 elements -> 4 operands of 8; 8-bit: 16 elements -> 2 operands.
 template <int WDT>
-__device__ __forceinline__ void dequant16(u32x4_t w, float s, bf16x8_t out[4]) {
-  if constexpr (WDT == W_INT4) {
+__device__ __forceinline__ void dequant16(u32x4_t w, scale_t<WDT> s, bf16x8_t out[4]) {
+  if constexpr (WDT == W_NV4) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      uint32_t o[4];
+      dq_nv4_word(w[j], j < 2 ? s.lo : s.hi, o);
+      out[j] = as_bf16x8(o[0], o[1], o[2], o[3]);
+    }
+  } else if constexpr (WDT == W_INT4) {
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       uint32_t o[4];
@@ -76,20 +99,26 @@ __device__ __forceinline__ void dequant16(u32x4_t w, float s, bf16x8_t out[4]) {
 // ---------------------------------------------------------------------------
 // Scales loaded ahead of use are kept as raw bits and converted at the use:
 // converting next to the load would make the wave wait for it there.
+// NVFP4: idx is the first of the chunk's two blocks (even), whose two E4M3
+// codes are read as one 16-bit word.
 template <int WDT>
 __device__ __forceinline__ uint32_t scale_raw_of(__amdgpu_buffer_rsrc_t r, uint32_t idx) {
   if constexpr (WDT == W_INT4) return __builtin_amdgcn_raw_buffer_load_b16(r, (int)(idx * 2), 0, 0);
   else if constexpr (WDT == W_FP4) return __builtin_amdgcn_raw_buffer_load_b8(r, (int)idx, 0, 0);
+  else if constexpr (WDT == W_NV4) return __builtin_amdgcn_raw_buffer_load_b16(r, (int)idx, 0, 0);
   else return 0u;
 }
 template <int WDT>
-__device__ __forceinline__ float scale_from_raw(uint32_t raw) {
+__device__ __forceinline__ scale_t<WDT> scale_from_raw(uint32_t raw) {
   if constexpr (WDT == W_INT4) return bf16_to_f32(raw);
   else if constexpr (WDT == W_FP4) return e8m0_as_scale(raw);
-  else return 1.0f;
+  else if constexpr (WDT == W_NV4) {
+    const uint32_t p = dq_fp8_pair<false>(raw);            // both E4M3 codes, exact in bf16
+    return Sc2{bf16_lo(p), bf16_hi(p)};
+  } else return 1.0f;
 }
 template <int WDT>
-__device__ __forceinline__ float scale_of(__amdgpu_buffer_rsrc_t r, uint32_t idx) {
+__device__ __forceinline__ scale_t<WDT> scale_of(__amdgpu_buffer_rsrc_t r, uint32_t idx) {
   return scale_from_raw<WDT>(scale_raw_of<WDT>(r, idx));
 }
 
@@ -102,14 +131,14 @@ __device__ __forceinline__ float scale_of(__amdgpu_buffer_rsrc_t r, uint32_t idx
 template <int WDT, int TN, int NSTEP, bool XLDS>
 __global__ __launch_bounds__(512) void k_gemv(const uint16_t* __restrict__ x, int M, int64_t N, int64_t K,
                                              const uint8_t* __restrict__ w, const void* __restrict__ sc,
-                                             int group_shift, const float* __restrict__ chscale,
+                                             int group_shift, const float* __restrict__ chscale, float alpha,
                                              uint16_t* __restrict__ y, int niter) {
   constexpr int EPL = WTraits<WDT>::bits == 4 ? 32 : 16;   // elements per lane per step
   constexpr int KSTEP = 4 * EPL;                            // K covered by a wave per step
   constexpr int KCH = NSTEP * KSTEP;                        // K per wave per chunk
   constexpr int MF = EPL / 8;                               // MFMAs per step per tile
   constexpr int BPE2 = WTraits<WDT>::bits == 4 ? 1 : 2;     // bytes per 2 elements
-  constexpr int SB = WDT == W_INT4 ? 2 : 1;                 // bytes per scale
+  constexpr int SB = scale_bytes<WDT>();
   constexpr int XW = 4 * KCH * 2 + 64;                      // per-wave x region (up to 4 rows)
   static_assert(KCH == 512 || !XLDS || KCH < 512, "x staging uses one 16-byte chunk per lane per 512 k");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -120,7 +149,7 @@ __global__ __launch_bounds__(512) void k_gemv(const uint16_t* __restrict__ x, in
   const int64_t n0 = (int64_t)blockIdx.x * 16 * TN;
   const uint32_t rowbytes = (uint32_t)(K * BPE2 / 2);
   const int64_t nrows = N - n0 < 16 * TN ? N - n0 : 16 * TN;
-  const int gs = WDT == W_INT4 ? group_shift : 5;            // log2 of the scale group
+  const int gs = gshift_of<WDT>(group_shift);               // log2 of the scale group
   const uint32_t spr = (uint32_t)(K >> gs);                  // scales per row
   const auto rw = make_rsrc(w + n0 * rowbytes, nrows * rowbytes);
   const auto rs = make_rsrc(reinterpret_cast<const uint8_t*>(sc) + (WDT == W_FP8 ? 0 : n0 * spr * SB),
@@ -147,7 +176,7 @@ __global__ __launch_bounds__(512) void k_gemv(const uint16_t* __restrict__ x, in
       for (int r = 0; r < 4; r++)
         if (r < M && lane < KCH / 8) xst[r] = bld16(rx, (uint32_t)(r * (uint32_t)K + k0 + 8 * lane) * 2);
     }
-    float sv[NSTEP][TN];
+    scale_t<WDT> sv[NSTEP][TN];
     u32x4_t wr[NSTEP][TN];
 #pragma unroll
     for (int c = 0; c < NSTEP; c++)
@@ -212,7 +241,7 @@ __global__ __launch_bounds__(512) void k_gemv(const uint16_t* __restrict__ x, in
     if (m >= M || col >= N) continue;
     float s = 0.0f;
     for (int wv = 0; wv < S; wv++) s += red[((wv * TN + t) * 16 + m) * 16 + n];
-    if constexpr (WDT == W_FP8) s *= chscale[col];
+    s *= WDT == W_FP8 ? chscale[col] * alpha : alpha;
     y[(int64_t)m * N + col] = (uint16_t)f32_to_bf16_bits(s);
   }
 }
@@ -253,7 +282,7 @@ __device__ __forceinline__ int bswz(int r) { return LPR == 2 ? (r >> 2) & 1 : (r
 template <int WDT>
 __global__ __launch_bounds__(512) void k_gemm8(const uint16_t* __restrict__ x, int64_t M, int64_t N, int64_t K,
                                               const uint8_t* __restrict__ w, const void* __restrict__ sc,
-                                              int group_shift, const float* __restrict__ chscale,
+                                              int group_shift, const float* __restrict__ chscale, float alpha,
                                               uint16_t* __restrict__ y, int tiles_m, int tiles_n) {
   using C = Gemm8<WDT>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -310,22 +339,21 @@ __global__ __launch_bounds__(512) void k_gemm8(const uint16_t* __restrict__ x, i
   // Scales are prefetched one step ahead as raw bits and converted only after
   // the next step's wait: converting at the load would make the wave wait for
   // the tile loads issued just before it.
-  const int gs = WDT == W_INT4 ? group_shift : 5;
+  const int gs = gshift_of<WDT>(group_shift);
   auto scale_raw = [&](int j, int64_t k0) -> uint32_t {
     const int64_t kk = (k0 + 32 * h) >> gs;
     if constexpr (WDT == W_INT4) {
       return reinterpret_cast<const uint16_t*>(sc)[srow[j] * (K >> gs) + kk];
     } else if constexpr (WDT == W_FP4) {
       return reinterpret_cast<const uint8_t*>(sc)[srow[j] * (K >> 5) + kk];
+    } else if constexpr (WDT == W_NV4) {
+      // the two blocks of the lane's 32 elements: an even byte offset
+      return *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(sc) + srow[j] * (K >> 4) + kk);
     } else {
       return 0u;
     }
   };
-  auto scale_val = [](uint32_t raw) -> float {
-    if constexpr (WDT == W_INT4) return __uint_as_float(raw << 16);
-    else if constexpr (WDT == W_FP4) return e8m0_as_scale(raw);
-    else return 1.0f;
-  };
+  auto scale_val = [](uint32_t raw) -> scale_t<WDT> { return scale_from_raw<WDT>(raw); };
 
   f32x16_t acc[4][2];
 #pragma unroll
@@ -359,7 +387,7 @@ __global__ __launch_bounds__(512) void k_gemm8(const uint16_t* __restrict__ x, i
   tile_barrier();
 
   // quarter q (k16 slice q) of a step's W fragments for both column subtiles
-  auto dequant_q = [&](const uint8_t* B, int q, const float (&cs)[2], bf16x8_t (&out)[4][2]) {
+  auto dequant_q = [&](const uint8_t* B, int q, const scale_t<WDT> (&cs)[2], bf16x8_t (&out)[4][2]) {
 #pragma unroll
     for (int j = 0; j < 2; j++) {
       const int br = wn * 64 + 32 * j + l32;
@@ -369,6 +397,7 @@ __global__ __launch_bounds__(512) void k_gemm8(const uint16_t* __restrict__ x, i
         const uint32_t wd = *reinterpret_cast<const uint32_t*>(bp + 16 * (h ^ sw) + 4 * q);
         uint32_t o[4];
         if constexpr (WDT == W_INT4) dq_int4_word(wd, cs[j], o);
+        else if constexpr (WDT == W_NV4) dq_nv4_word(wd, q < 2 ? cs[j].lo : cs[j].hi, o);
         else dq_fp4_word(wd, cs[j], o);
         out[q][j] = as_bf16x8(o[0], o[1], o[2], o[3]);
       } else {
@@ -380,7 +409,7 @@ __global__ __launch_bounds__(512) void k_gemm8(const uint16_t* __restrict__ x, i
   };
   bf16x8_t ba[4][2], bb[4][2];
   {
-    float c0[2];
+    scale_t<WDT> c0[2];
 #pragma unroll
     for (int j = 0; j < 2; j++) c0[j] = scale_val(sa[j]);
 #pragma unroll
@@ -392,7 +421,7 @@ __global__ __launch_bounds__(512) void k_gemm8(const uint16_t* __restrict__ x, i
                   uint32_t (&sload)[2]) {
     const int st1 = stage == 2 ? 0 : stage + 1;
     const int st2 = st1 == 2 ? 0 : st1 + 1;
-    float cn[2];
+    scale_t<WDT> cn[2];
 #pragma unroll
     for (int j = 0; j < 2; j++) cn[j] = scale_val(snext[j]);
     if (kt + 2 < nk) {
@@ -436,8 +465,8 @@ __global__ __launch_bounds__(512) void k_gemm8(const uint16_t* __restrict__ x, i
 #pragma unroll
   for (int j = 0; j < 2; j++) {
     const int64_t col = n0 + wn * 64 + 32 * j + l32;
-    cs[j] = 1.0f;
-    if constexpr (WDT == W_FP8) cs[j] = col < N ? chscale[col] : 0.0f;
+    cs[j] = alpha;
+    if constexpr (WDT == W_FP8) cs[j] = col < N ? chscale[col] * alpha : 0.0f;
     cb[j] = col < N ? (uint32_t)(col * 2) : 0x80000000u;    // columns past N: out of range
   }
 #pragma unroll
@@ -486,7 +515,7 @@ template <int WDT, int SPW, int R, int NW>
 __global__ __launch_bounds__(64 * NW) void k_gemv_ring(const uint16_t* __restrict__ x, int M, int64_t N, int64_t K,
                                                   const uint8_t* __restrict__ w, const void* __restrict__ sc,
                                                   int group_shift, const float* __restrict__ chscale,
-                                                  uint16_t* __restrict__ y) {
+                                                  float alpha, uint16_t* __restrict__ y) {
   constexpr int EPL = WTraits<WDT>::bits == 4 ? 32 : 16;
   constexpr int KSTEP = 4 * EPL;
   constexpr int KSL = SPW * KSTEP;                            // K of one wave's slice
@@ -501,9 +530,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_ring(const uint16_t* __restric
   const int64_t n0 = (int64_t)blockIdx.x * 16;
   const uint32_t rowbytes = (uint32_t)(K * BPE2 / 2);
   const int64_t nrows = N - n0 < 16 ? N - n0 : 16;
-  const int gs = WDT == W_INT4 ? group_shift : 5;
+  const int gs = gshift_of<WDT>(group_shift);
   const uint32_t spr = (uint32_t)(K >> gs);                  // scales per row
-  constexpr int SB = WDT == W_INT4 ? 2 : 1;                   // bytes per scale
+  constexpr int SB = scale_bytes<WDT>();
   const uint32_t sbrow = (uint32_t)(KSL >> gs) * SB;         // scale bytes per row of the slice
   const auto rw = make_rsrc(w + n0 * rowbytes, nrows * rowbytes);
   const auto rs = make_rsrc(reinterpret_cast<const uint8_t*>(sc) + (WDT == W_FP8 ? 0 : n0 * spr * SB),
@@ -526,9 +555,13 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_ring(const uint16_t* __restric
   uint32_t svr[SPW];
   if constexpr (WDT != W_FP8) {
     if (sdma) {
+      // 16 rows x cpr chunks; one DMA instruction moves 64 of them (1 KB)
       const int cpr = (int)srs / 16;
-      if (lane < 16 * cpr)
-        lds_dma16(rs, sl, (uint32_t)(lane / cpr) * spr * SB + (kbase >> gs) * SB + 16 * (lane % cpr));
+      for (int q = 0; q < (16 * cpr + 63) / 64; q++) {
+        const int L = 64 * q + lane;
+        if (L < 16 * cpr)
+          lds_dma16(rs, sl + 1024 * q, (uint32_t)(L / cpr) * spr * SB + (kbase >> gs) * SB + 16 * (L % cpr));
+      }
     } else {
 #pragma unroll
       for (int c = 0; c < SPW; c++)
@@ -567,13 +600,16 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_ring(const uint16_t* __restric
       }
     }
     const u32x4_t wv = *reinterpret_cast<const u32x4_t*>(ring + (c % R) * 1024 + lane * 16);
-    float scv = 1.0f;
+    scale_t<WDT> scv{};
     if constexpr (WDT == W_INT4) {
       const uint32_t gi = (uint32_t)(c * KSTEP + EPL * g) >> gs;
       scv = sdma ? bf16_to_f32(*reinterpret_cast<const uint16_t*>(sl + nl * srs + 2 * gi)) : scale_from_raw<WDT>(svr[c]);
     } else if constexpr (WDT == W_FP4) {
       const uint32_t gi = (uint32_t)(c * KSTEP + EPL * g) >> 5;
       scv = sdma ? e8m0_as_scale(sl[nl * srs + gi]) : scale_from_raw<WDT>(svr[c]);
+    } else if constexpr (WDT == W_NV4) {
+      const uint32_t gi = (uint32_t)(c * KSTEP + EPL * g) >> 4;
+      scv = scale_from_raw<WDT>(sdma ? (uint32_t)*reinterpret_cast<const uint16_t*>(sl + nl * srs + gi) : svr[c]);
     }
     bf16x8_t xa[MF];
 #pragma unroll
@@ -600,7 +636,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_ring(const uint16_t* __restric
       float s = 0.0f;
 #pragma unroll
       for (int wv = 0; wv < NW; wv++) s += red[(wv * 16 + m) * 16 + n];
-      if constexpr (WDT == W_FP8) s *= chscale[col];
+      s *= WDT == W_FP8 ? chscale[col] * alpha : alpha;
       y[(int64_t)m * N + col] = (uint16_t)f32_to_bf16_bits(s);
     }
   }
@@ -620,23 +656,23 @@ inline GemvSplit gemv_split(int64_t T, int maxstep) {
 
 template <int WDT, int TN, int NSTEP, bool XLDS>
 void gemv_go(const GemvSplit& sp, const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w,
-             const void* sc, int group, const float* ch, uint16_t* y, hipStream_t s) {
+             const void* sc, int group, const float* ch, float alpha, uint16_t* y, hipStream_t s) {
   const unsigned grid = (unsigned)((N + 16 * TN - 1) / (16 * TN));
   constexpr int KCH = NSTEP * (WTraits<WDT>::bits == 4 ? 128 : 64);
   const size_t lds = (XLDS ? (size_t)sp.S * (4 * KCH * 2 + 64) : 0) + (size_t)sp.S * TN * 1024;
   const int gshift = group == 32 ? 5 : group == 64 ? 6 : 7;
-  k_gemv<WDT, TN, NSTEP, XLDS><<<grid, 64 * sp.S, lds, s>>>(x, (int)M, N, K, w, sc, gshift, ch, y, sp.niter);
+  k_gemv<WDT, TN, NSTEP, XLDS><<<grid, 64 * sp.S, lds, s>>>(x, (int)M, N, K, w, sc, gshift, ch, alpha, y, sp.niter);
 }
 
 template <int WDT, int TN, bool XLDS>
 void gemv_nstep(const GemvSplit& sp, const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w,
-                const void* sc, int group, const float* ch, uint16_t* y, hipStream_t s) {
+                const void* sc, int group, const float* ch, float alpha, uint16_t* y, hipStream_t s) {
   switch (sp.nstep) {
-    case 8: if constexpr (WTraits<WDT>::bits == 8) { gemv_go<WDT, TN, 8, XLDS>(sp, x, M, N, K, w, sc, group, ch, y, s); break; }
+    case 8: if constexpr (WTraits<WDT>::bits == 8) { gemv_go<WDT, TN, 8, XLDS>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s); break; }
             [[fallthrough]];
-    case 4: gemv_go<WDT, TN, 4, XLDS>(sp, x, M, N, K, w, sc, group, ch, y, s); break;
-    case 2: gemv_go<WDT, TN, 2, XLDS>(sp, x, M, N, K, w, sc, group, ch, y, s); break;
-    default: gemv_go<WDT, TN, 1, XLDS>(sp, x, M, N, K, w, sc, group, ch, y, s); break;
+    case 4: gemv_go<WDT, TN, 4, XLDS>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s); break;
+    case 2: gemv_go<WDT, TN, 2, XLDS>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s); break;
+    default: gemv_go<WDT, TN, 1, XLDS>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s); break;
   }
 }
 
@@ -650,7 +686,8 @@ template <int WDT, int SPW, int R, int NW>
 __global__ __launch_bounds__(64 * NW) void k_gemv_ring16(const uint16_t* __restrict__ x, int M, int64_t N,
                                                     int64_t K, const uint8_t* __restrict__ w,
                                                     const void* __restrict__ sc, int group_shift,
-                                                    const float* __restrict__ chscale, uint16_t* __restrict__ y) {
+                                                    const float* __restrict__ chscale, float alpha,
+                                                    uint16_t* __restrict__ y) {
   constexpr int EPL = WTraits<WDT>::bits == 4 ? 32 : 16;
   constexpr int KSTEP = 4 * EPL;
   constexpr int KSL = SPW * KSTEP;
@@ -671,9 +708,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_ring16(const uint16_t* __restr
   const int64_t n0 = (int64_t)blockIdx.x * 16;
   const uint32_t rowbytes = (uint32_t)(K * BPE2 / 2);
   const int64_t nrows = N - n0 < 16 ? N - n0 : 16;
-  const int gs = WDT == W_INT4 ? group_shift : 5;
+  const int gs = gshift_of<WDT>(group_shift);
   const uint32_t spr = (uint32_t)(K >> gs);
-  constexpr int SB = WDT == W_INT4 ? 2 : 1;
+  constexpr int SB = scale_bytes<WDT>();
   const auto rw = make_rsrc(w + n0 * rowbytes, nrows * rowbytes);
   const auto rs = make_rsrc(reinterpret_cast<const uint8_t*>(sc) + (WDT == W_FP8 ? 0 : n0 * spr * SB),
                             WDT == W_FP8 ? 0 : nrows * spr * SB);
@@ -717,7 +754,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_ring16(const uint16_t* __restr
       const int ch = (EPL / 8) * g + j;
       xa[j] = as_bf16x8(ld16(b + 1024 + nl * XRB + 16 * (ch ^ (nl & (CPR - 1)))));
     }
-    const float scv = WDT == W_FP8 ? 1.0f : scale_from_raw<WDT>(svr[c]);
+    const scale_t<WDT> scv = scale_from_raw<WDT>(WDT == W_FP8 ? 0u : svr[c]);
     bf16x8_t bq[4];
     dequant16<WDT>(wv, scv, bq);
     if (c + R < SPW) {
@@ -741,7 +778,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_ring16(const uint16_t* __restr
       float s = 0.0f;
 #pragma unroll
       for (int wv = 0; wv < NW; wv++) s += red[(wv * 16 + m) * 16 + n];
-      if constexpr (WDT == W_FP8) s *= chscale[col];
+      s *= WDT == W_FP8 ? chscale[col] * alpha : alpha;
       y[(int64_t)m * N + col] = (uint16_t)f32_to_bf16_bits(s);
     }
   }
@@ -754,7 +791,7 @@ constexpr int RING_NW = 4;
 constexpr int RING_DEPTH = 2;
 template <int WDT, int SPW>
 wq_status ring16_go(int64_t M, const uint16_t* x, int64_t N, int64_t K, const uint8_t* w, const void* sc, int gshift,
-                    const float* ch, uint16_t* y, hipStream_t s) {
+                    const float* ch, float alpha, uint16_t* y, hipStream_t s) {
   constexpr int R = SPW < 2 ? SPW : 2;
   if constexpr (R < 2) {
     return WQ_EUNSUPPORTED;
@@ -763,18 +800,19 @@ wq_status ring16_go(int64_t M, const uint16_t* x, int64_t N, int64_t K, const ui
     const size_t lds = (size_t)RING_NW * R * (1024 + XSLOT);
     const unsigned grid = (unsigned)((N + 15) / 16);
     if (allow_lds<k_gemv_ring16<WDT, SPW, R, RING_NW>>(lds) != hipSuccess) return WQ_EHIP;
-    k_gemv_ring16<WDT, SPW, R, RING_NW><<<grid, 64 * RING_NW, lds, s>>>(x, (int)M, N, K, w, sc, gshift, ch, y);
+    k_gemv_ring16<WDT, SPW, R, RING_NW><<<grid, 64 * RING_NW, lds, s>>>(x, (int)M, N, K, w, sc, gshift, ch, alpha,
+                                                                         y);
     return WQ_OK;
   }
 }
 
 template <int WDT, int SPW>
 wq_status ring_go(int64_t M, const uint16_t* x, int64_t N, int64_t K, const uint8_t* w, const void* sc, int gshift,
-             const float* ch, uint16_t* y, hipStream_t s) {
+                  const float* ch, float alpha, uint16_t* y, hipStream_t s) {
   constexpr int R0 = SPW < RING_DEPTH ? SPW : RING_DEPTH;
   constexpr int KSL = SPW * (WTraits<WDT>::bits == 4 ? 128 : 64);
-  const int gs = WDT == W_INT4 ? gshift : 5;
-  const int sbrow = (KSL >> gs) * (WDT == W_INT4 ? 2 : 1);
+  const int gs = gshift_of<WDT>(gshift);
+  const int sbrow = (KSL >> gs) * scale_bytes<WDT>();
   const int sbytes = WDT == W_FP8 ? 0 : 16 * (sbrow < 16 ? 16 : sbrow);
   const unsigned grid = (unsigned)((N + 15) / 16);
   auto lds_for = [&](int r) { return (size_t)RING_NW * (r * 1024 + M * KSL * 2 + ((sbytes + 15) & ~15)); };
@@ -783,17 +821,19 @@ wq_status ring_go(int64_t M, const uint16_t* x, int64_t N, int64_t K, const uint
   if (R0 >= 7 && lds_for(R0) > budget && lds_for(R0 - 1) <= budget) {
     constexpr int R = R0 >= 7 ? R0 - 1 : R0;
     if (allow_lds<k_gemv_ring<WDT, SPW, R, RING_NW>>(lds_for(R)) != hipSuccess) return WQ_EHIP;
-    k_gemv_ring<WDT, SPW, R, RING_NW><<<grid, 64 * RING_NW, lds_for(R), s>>>(x, (int)M, N, K, w, sc, gshift, ch, y);
+    k_gemv_ring<WDT, SPW, R, RING_NW><<<grid, 64 * RING_NW, lds_for(R), s>>>(x, (int)M, N, K, w, sc, gshift, ch, alpha,
+                                                                                   y);
   } else {
     if (allow_lds<k_gemv_ring<WDT, SPW, R0, RING_NW>>(lds_for(R0)) != hipSuccess) return WQ_EHIP;
-    k_gemv_ring<WDT, SPW, R0, RING_NW><<<grid, 64 * RING_NW, lds_for(R0), s>>>(x, (int)M, N, K, w, sc, gshift, ch, y);
+    k_gemv_ring<WDT, SPW, R0, RING_NW><<<grid, 64 * RING_NW, lds_for(R0), s>>>(x, (int)M, N, K, w, sc, gshift, ch, alpha,
+                                                                                    y);
   }
   return WQ_OK;
 }
 
 template <int WDT>
 wq_status launch_gemv(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w, const void* sc, int group,
-                      const float* ch, uint16_t* y, hipStream_t s) {
+                      const float* ch, float alpha, uint16_t* y, hipStream_t s) {
   constexpr int KSTEP = WTraits<WDT>::bits == 4 ? 128 : 64;
   const int gshift = group == 32 ? 5 : group == 64 ? 6 : 7;
   if (M <= 4 && K % (KSTEP * RING_NW) == 0 && 16 * K * 2 <= 0x7FFFFFF0LL) {
@@ -801,11 +841,11 @@ wq_status launch_gemv(const uint16_t* x, int64_t M, int64_t N, int64_t K, const 
     if (spw == 1 || spw == 2 || spw == 4 || spw == 8 || spw == 16) {
       wq_status st;
       switch (spw) {
-        case 1: st = ring_go<WDT, 1>(M, x, N, K, w, sc, gshift, ch, y, s); break;
-        case 2: st = ring_go<WDT, 2>(M, x, N, K, w, sc, gshift, ch, y, s); break;
-        case 4: st = ring_go<WDT, 4>(M, x, N, K, w, sc, gshift, ch, y, s); break;
-        case 8: st = ring_go<WDT, 8>(M, x, N, K, w, sc, gshift, ch, y, s); break;
-        default: st = ring_go<WDT, 16>(M, x, N, K, w, sc, gshift, ch, y, s); break;
+        case 1: st = ring_go<WDT, 1>(M, x, N, K, w, sc, gshift, ch, alpha, y, s); break;
+        case 2: st = ring_go<WDT, 2>(M, x, N, K, w, sc, gshift, ch, alpha, y, s); break;
+        case 4: st = ring_go<WDT, 4>(M, x, N, K, w, sc, gshift, ch, alpha, y, s); break;
+        case 8: st = ring_go<WDT, 8>(M, x, N, K, w, sc, gshift, ch, alpha, y, s); break;
+        default: st = ring_go<WDT, 16>(M, x, N, K, w, sc, gshift, ch, alpha, y, s); break;
       }
       return st != WQ_OK ? st : wq_launch_status();
     }
@@ -815,10 +855,10 @@ wq_status launch_gemv(const uint16_t* x, int64_t M, int64_t N, int64_t K, const 
     if (spw == 2 || spw == 4 || spw == 8 || spw == 16) {
       wq_status st;
       switch (spw) {
-        case 2: st = ring16_go<WDT, 2>(M, x, N, K, w, sc, gshift, ch, y, s); break;
-        case 4: st = ring16_go<WDT, 4>(M, x, N, K, w, sc, gshift, ch, y, s); break;
-        case 8: st = ring16_go<WDT, 8>(M, x, N, K, w, sc, gshift, ch, y, s); break;
-        default: st = ring16_go<WDT, 16>(M, x, N, K, w, sc, gshift, ch, y, s); break;
+        case 2: st = ring16_go<WDT, 2>(M, x, N, K, w, sc, gshift, ch, alpha, y, s); break;
+        case 4: st = ring16_go<WDT, 4>(M, x, N, K, w, sc, gshift, ch, alpha, y, s); break;
+        case 8: st = ring16_go<WDT, 8>(M, x, N, K, w, sc, gshift, ch, alpha, y, s); break;
+        default: st = ring16_go<WDT, 16>(M, x, N, K, w, sc, gshift, ch, alpha, y, s); break;
       }
       return st != WQ_OK ? st : wq_launch_status();
     }
@@ -832,22 +872,22 @@ wq_status launch_gemv(const uint16_t* x, int64_t M, int64_t N, int64_t K, const 
   }
   const GemvSplit sp = gemv_split(K / KSTEP, MAXSTEP);
   const bool xlds = M <= 4;
-  if (xlds) gemv_nstep<WDT, 1, true>(sp, x, M, N, K, w, sc, group, ch, y, s);
-  else if (M <= 4) gemv_nstep<WDT, 1, false>(sp, x, M, N, K, w, sc, group, ch, y, s);
-  else gemv_nstep<WDT, 2, false>(sp, x, M, N, K, w, sc, group, ch, y, s);
+  if (xlds) gemv_nstep<WDT, 1, true>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s);
+  else if (M <= 4) gemv_nstep<WDT, 1, false>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s);
+  else gemv_nstep<WDT, 2, false>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s);
   return wq_launch_status();
 }
 
 template <int WDT>
 wq_status launch_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w, const void* sc, int group,
-                      const float* ch, uint16_t* y, hipStream_t s) {
+                      const float* ch, float alpha, uint16_t* y, hipStream_t s) {
   using C8 = Gemm8<WDT>;
   // 32-bit buffer offsets: one 256-row x tile, one 256-row W tile, one 256-row y tile
   if ((int64_t)C8::BM * K * 2 > 0x7FFFFFF0LL || (int64_t)C8::BM * N * 2 > 0x7FFFFFF0LL) return WQ_EINVAL;
   if (allow_lds<k_gemm8<WDT>>(C8::LDS) != hipSuccess) return WQ_EHIP;
   const int tm = (int)((M + C8::BM - 1) / C8::BM), tn = (int)((N + C8::BN - 1) / C8::BN);
   const int gshift = group == 32 ? 5 : group == 64 ? 6 : 7;
-  k_gemm8<WDT><<<(unsigned)(tm * tn), 512, C8::LDS, s>>>(x, M, N, K, w, sc, gshift, ch, y, tm, tn);
+  k_gemm8<WDT><<<(unsigned)(tm * tn), 512, C8::LDS, s>>>(x, M, N, K, w, sc, gshift, ch, alpha, y, tm, tn);
   return wq_launch_status();
 }
 
@@ -858,17 +898,19 @@ extern "C" {
 size_t wq_gemm_workspace_size(int64_t, int64_t, int64_t, int, int32_t) { return 0; }
 
 wq_status wq_gemm(const void* x_bf16, int64_t M, int64_t N, int64_t K, const void* wqp, int w_dtype,
-                  const void* w_scales, int s_dtype, int32_t group, void* y_bf16, void* workspace, size_t ws_bytes,
-                  void* stream) {
+                  const void* w_scales, int s_dtype, int32_t group, float alpha, void* y_bf16, void* workspace,
+                  size_t ws_bytes, void* stream) {
   (void)workspace;
   (void)ws_bytes;
   if (!x_bf16 || !wqp || !w_scales || !y_bf16) return WQ_EINVAL;
   if (M <= 0 || N <= 0 || K <= 0 || K % 128) return WQ_EINVAL;
+  if (!(alpha == alpha) || alpha > 3.4028234e38f || alpha < -3.4028234e38f) return WQ_EINVAL;
   if (!wq_numel_ok(M, K) || !wq_numel_ok(N, K) || !wq_numel_ok(M, N) || M > 0x7FFFFFFF) return WQ_EINVAL;
   if (!wq_aligned(x_bf16) || !wq_aligned(wqp) || !wq_aligned(y_bf16)) return WQ_EALIGN;
   int wdt;
   if (w_dtype == WQ_INT4X8 && s_dtype == WQ_BF16 && (group == 32 || group == 64 || group == 128)) wdt = W_INT4;
   else if (w_dtype == WQ_E2M1X2 && s_dtype == WQ_E8M0 && group == 32) wdt = W_FP4;
+  else if (w_dtype == WQ_E2M1X2 && s_dtype == WQ_E4M3 && group == 16) wdt = W_NV4;
   else if (w_dtype == WQ_E4M3 && s_dtype == WQ_F32 && group == K) wdt = W_FP8;
   else return WQ_EUNSUPPORTED;
   if (M > 16 && (int64_t)((M + 255) / 256) * ((N + 255) / 256) > 0x7FFFFFFF) return WQ_EINVAL;   // prefill tiles
@@ -879,15 +921,17 @@ wq_status wq_gemm(const void* x_bf16, int64_t M, int64_t N, int64_t K, const voi
   const float* ch = wdt == W_FP8 ? (const float*)w_scales : nullptr;
   if (M <= 16) {
     switch (wdt) {
-      case W_INT4: return launch_gemv<W_INT4>(x, M, N, K, w, w_scales, group, ch, y, s);
-      case W_FP4: return launch_gemv<W_FP4>(x, M, N, K, w, w_scales, group, ch, y, s);
-      default: return launch_gemv<W_FP8>(x, M, N, K, w, w_scales, group, ch, y, s);
+      case W_INT4: return launch_gemv<W_INT4>(x, M, N, K, w, w_scales, group, ch, alpha, y, s);
+      case W_FP4: return launch_gemv<W_FP4>(x, M, N, K, w, w_scales, group, ch, alpha, y, s);
+      case W_NV4: return launch_gemv<W_NV4>(x, M, N, K, w, w_scales, group, ch, alpha, y, s);
+      default: return launch_gemv<W_FP8>(x, M, N, K, w, w_scales, group, ch, alpha, y, s);
     }
   }
   switch (wdt) {
-    case W_INT4: return launch_gemm<W_INT4>(x, M, N, K, w, w_scales, group, ch, y, s);
-    case W_FP4: return launch_gemm<W_FP4>(x, M, N, K, w, w_scales, group, ch, y, s);
-    default: return launch_gemm<W_FP8>(x, M, N, K, w, w_scales, group, ch, y, s);
+    case W_INT4: return launch_gemm<W_INT4>(x, M, N, K, w, w_scales, group, ch, alpha, y, s);
+    case W_FP4: return launch_gemm<W_FP4>(x, M, N, K, w, w_scales, group, ch, alpha, y, s);
+    case W_NV4: return launch_gemm<W_NV4>(x, M, N, K, w, w_scales, group, ch, alpha, y, s);
+    default: return launch_gemm<W_FP8>(x, M, N, K, w, w_scales, group, ch, alpha, y, s);
   }
 }
 

@@ -1,5 +1,5 @@
 // Block-scaled quantizers (fp32/bf16 -> E4M3, MXFP4, MX with a choice of scale
-// rule and E2M1 or E4M3 elements, INT4) and the dequantizer
+// rule and E2M1 or E4M3 elements, NVFP4, INT4) and the dequantizer
 // entry point, for gfx950.  Memory-bound: every thread moves 16-byte vectors;
 // block maxima are reduced across the lanes that share a block with xor
 // shuffles.
@@ -224,6 +224,57 @@ __global__ __launch_bounds__(kThreads) void k_mx(const void* __restrict__ x, int
 }
 
 // ---------------------------------------------------------------------------
+// NVFP4: one 16-element block per thread.  Block scale e4m3(RN(RN(amax/6)/g))
+// (two correctly rounded divisions), elements RN(x / d) with d = e4m3 value * g
+// the dequantized scale, clamped to +-6 and converted with an unscaled E2M1
+// conversion (quotients beyond 16 only need their sign).  A zero d gives zeros
+// with the sign of x.
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_nvfp4(const void* __restrict__ x, int64_t nblocks, float g,
+                                                   uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (t >= nblocks) return;
+  float v[16];
+  load8<BF16>(x, t * 16, v);
+  load8<BF16>(x, t * 16 + 8, v + 8);
+  const float m = __builtin_fmaxf(absmax8(v), absmax8(v + 8));
+  const float sq = (m / 6.0f) / g;
+  const uint32_t s8 = e4m3_pack2<false>(clamp448(sq), 0.0f, 0u) & 0xFFu;
+  const float d = bf16_lo(dq_fp8_pair<false>(s8)) * g;
+  float q[16];
+  if (d >= 0x1p-90f && d <= 0x1p90f) {
+    // a saturated scale can leave quotients far above 6 (even past fp32): the
+    // first estimate decides those (the correction step would turn an
+    // infinite estimate into NaN)
+    const float y = 1.0f / d;
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      const float q0 = v[i] * y;
+      q[i] = __builtin_fabsf(q0) > 16.0f ? q0 : div_rn_markstein(v[i], d, y);
+    }
+  } else if (d > 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 16; i++) q[i] = v[i] / d;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; i++) q[i] = __builtin_copysignf(0.0f, v[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; i++) q[i] = __builtin_fminf(__builtin_fmaxf(q[i], -6.0f), 6.0f);
+  uint32_t w0 = e2m1_pack2<0>(0u, q[0], q[1], 1.0f);
+  w0 = e2m1_pack2<1>(w0, q[2], q[3], 1.0f);
+  w0 = e2m1_pack2<2>(w0, q[4], q[5], 1.0f);
+  w0 = e2m1_pack2<3>(w0, q[6], q[7], 1.0f);
+  uint32_t w1 = e2m1_pack2<0>(0u, q[8], q[9], 1.0f);
+  w1 = e2m1_pack2<1>(w1, q[10], q[11], 1.0f);
+  w1 = e2m1_pack2<2>(w1, q[12], q[13], 1.0f);
+  w1 = e2m1_pack2<3>(w1, q[14], q[15], 1.0f);
+  *reinterpret_cast<u32x2_t*>(codes + t * 8) = u32x2_t{w0, w1};
+  scales[t] = (uint8_t)s8;
+}
+
+// ---------------------------------------------------------------------------
 // INT4 symmetric groups: 16 elements per thread, group/16 lanes per group.
 // ---------------------------------------------------------------------------
 template <bool BF16>
@@ -280,6 +331,19 @@ __global__ __launch_bounds__(kThreads) void k_dq_fp4(const uint32_t* __restrict_
   const float sc = e8m0_as_scale(scales[n * (K / block) + k / block]);
   uint32_t o[4];
   dq_fp4_word(codes[t], sc, o);
+  *reinterpret_cast<u32x4_t*>(out + e) = u32x4_t{o[0], o[1], o[2], o[3]};
+}
+
+// NVFP4 operand: E2M1 word times its block's E4M3 scale value (exact in bf16).
+__global__ __launch_bounds__(kThreads) void k_dq_nv4(const uint32_t* __restrict__ codes,
+                                                    const uint8_t* __restrict__ scales, int64_t nchunks, int64_t K,
+                                                    uint16_t* __restrict__ out) {
+  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (t >= nchunks) return;
+  const int64_t e = t * 8, n = e / K, k = e % K;
+  const float sc = bf16_lo(dq_fp8_pair<false>(scales[n * (K / 16) + k / 16]));
+  uint32_t o[4];
+  dq_nv4_word(codes[t], sc, o);
   *reinterpret_cast<u32x4_t*>(out + e) = u32x4_t{o[0], o[1], o[2], o[3]};
 }
 
@@ -366,6 +430,20 @@ wq_status quantize_mx(const void* x, int x_dtype, int64_t rows, int64_t cols, in
   return wq_launch_status();
 }
 
+wq_status quantize_nvfp4(const void* x, int x_dtype, int64_t rows, int64_t cols, float tensor_scale,
+                         uint8_t* codes, uint8_t* scales, void* stream) {
+  if (!x || !codes || !scales || rows <= 0 || cols <= 0 || cols % 16) return WQ_EINVAL;
+  if (x_dtype != WQ_F32 && x_dtype != WQ_BF16) return WQ_EUNSUPPORTED;
+  if (!(tensor_scale > 0.0f) || !(tensor_scale <= 3.4028234e38f)) return WQ_EINVAL;
+  if (!wq_numel_ok(rows, cols)) return WQ_EINVAL;
+  if (!wq_aligned(x) || !wq_aligned(codes) || !wq_aligned(scales)) return WQ_EALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t nb = rows * cols / 16;
+  if (x_dtype == WQ_BF16) k_nvfp4<true><<<grid_for(nb), kThreads, 0, s>>>(x, nb, tensor_scale, codes, scales);
+  else k_nvfp4<false><<<grid_for(nb), kThreads, 0, s>>>(x, nb, tensor_scale, codes, scales);
+  return wq_launch_status();
+}
+
 wq_status quantize_int4(const void* w, int w_dtype, int64_t rows, int64_t cols, int32_t group, uint32_t* packed,
                         uint16_t* scales, void* stream) {
   if (!w || !packed || !scales || rows <= 0 || cols <= 0) return WQ_EINVAL;
@@ -393,6 +471,12 @@ wq_status wq_dequant(const void* wqp, int w_dtype, const void* w_scales, int s_d
     if (K % group) return WQ_EINVAL;
     k_dq_int4<<<grid_for(nch), kThreads, 0, s>>>((const uint32_t*)wqp, (const uint16_t*)w_scales, nch, K, group,
                                                   w_bf16);
+    return wq_launch_status();
+  }
+  if (w_dtype == WQ_E2M1X2 && s_dtype == WQ_E4M3) {
+    if (group != 16) return WQ_EUNSUPPORTED;
+    if (!w_scales) return WQ_EINVAL;
+    k_dq_nv4<<<grid_for(nch), kThreads, 0, s>>>((const uint32_t*)wqp, (const uint8_t*)w_scales, nch, K, w_bf16);
     return wq_launch_status();
   }
   if (w_dtype == WQ_E2M1X2) {
