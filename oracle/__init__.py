@@ -29,6 +29,7 @@ mx        MX block quantizers under five E8M0 rules (exponent-first with the
           elements
 nvfp4     NVFP4: E2M1 blocks of 16 with an E4M3 scale and a per-tensor fp32 scale
 int4      symmetric INT4 group quantizer with bf16 scales
+int4_asym asymmetric INT4: unsigned codes, bf16 group scale, integer zero-point
 dequant   packed weights + scales -> bf16 operands
 gemm      fp64 reference matmul and the acceptance bound
 w4a8      MoE routing, W4A8 scale recipe, INT4 -> E4M3 lookup table, grouped GEMM
