@@ -14,8 +14,8 @@ synchronisation; `value` is algorithmic bytes / time.
 
 The same JSON line carries the roofline of that kernel (HIP events over the
 timed region on the launch stream), the oracle timed on the host (`cpu_baseline`)
-and `secondary` measurements: decode at M = 4 and 16, W8A16, NVFP4 decode at
-M = 1 and 16, prefill MXFP4 and NVFP4 at M = 8192 (TFLOP/s), the activation
+and `secondary` measurements: decode at M = 4 and 16, W8A16, asymmetric INT4
+decode at M = 1, NVFP4 decode at M = 1 and 16, prefill MXFP4 and NVFP4 at M = 8192 (TFLOP/s), the activation
 quantizers at 4096 x 7168 (E4M3 per 128, MXFP4 per 16, MXFP8 per 32 under two
 E8M0 rules, and the share of blocks whose maximum clips under each rule), the
 MXFP4 weight quantizer, the W4A8 mixture-of-experts grouped GEMMs (gate/up and
@@ -24,7 +24,7 @@ torch.matmul (hipBLASLt) at the prefill shape as secondary denominators.
 
 --only CASE runs a single case without the full summary (for rocprofv3):
 decode (the same graph-timed steps as the headline, prints one short JSON
-line), decode_w8, decode_nvfp4, prefill, prefill_nvfp4, quant_e4m3, quant_mxfp4, quant_mxfp8, wquant_mxfp4, copy,
+line), decode_w8, decode_nvfp4, decode_asym, prefill, prefill_nvfp4, quant_e4m3, quant_mxfp4, quant_mxfp8, wquant_mxfp4, copy,
 moe_gate_up, moe_down.
 """
 from __future__ import annotations
@@ -141,8 +141,9 @@ def nvfp4_tensor_scale(torch, w):
 
 
 class Decode:
-    """x[M, 4096] . dequant(W[14336, 4096])^T, INT4 g128, E4M3 per-channel or
-    NVFP4 (E4M3 scale per 16, per-tensor fp32 scale)."""
+    """x[M, 4096] . dequant(W[14336, 4096])^T, INT4 g128 (symmetric, or
+    asymmetric with a zero-point), E4M3 per-channel or NVFP4 (E4M3 scale per
+    16, per-tensor fp32 scale)."""
 
     def __init__(self, torch, W, M, kind="int4", K=4096, N=14336):
         from synthetic import decode_inputs
@@ -156,6 +157,11 @@ class Decode:
             self.wbytes = packed.numel() * 4 + sb.numel() * 2
             base = (packed, sb)
             self.meta = (W.WQ_INT4X8, W.WQ_BF16, 128)
+        elif kind == "int4_asym":
+            packed, sz = W.quantize_int4_asym(wdev, 128)
+            self.wbytes = packed.numel() * 4 + sz.numel() * 4
+            base = (packed, sz)
+            self.meta = (W.WQ_UINT4X8, W.WQ_BF16Z, 128)
         elif kind == "nvfp4":
             self.alpha = nvfp4_tensor_scale(torch, wdev)
             codes, sc = W.quantize_nvfp4(wdev, self.alpha)
@@ -366,6 +372,7 @@ def main():
     if args.only and args.only != "decode":
         case = args.only
         mk = {"decode_w8": lambda: Decode(torch, W, 1, "e4m3"), "decode_nvfp4": lambda: Decode(torch, W, 1, "nvfp4"),
+              "decode_asym": lambda: Decode(torch, W, 1, "int4_asym"),
               "prefill_nvfp4": lambda: Prefill(torch, W, kind="nvfp4"),
               "prefill": lambda: Prefill(torch, W), "quant_e4m3": lambda: ActQuant(torch, W, "e4m3"),
               "quant_mxfp4": lambda: ActQuant(torch, W, "mxfp4"), "copy": lambda: Copy(torch),
@@ -414,6 +421,7 @@ def main():
     add_decode("decode_w4a16_m4", 4, "int4")
     add_decode("decode_w4a16_m16", 16, "int4")
     add_decode("decode_w8a16_m1", 1, "e4m3")
+    add_decode("decode_w4a16_asym_m1", 1, "int4_asym")
     add_decode("decode_nvfp4_m1", 1, "nvfp4")
     add_decode("decode_nvfp4_m16", 16, "nvfp4")
     torch.cuda.empty_cache()

@@ -26,6 +26,11 @@
  *            bits 4j..4j+3 of word i.
  * WQ_BF16    bfloat16 bit patterns (uint16).
  * WQ_F32     IEEE binary32.
+ * WQ_UINT4X8 unsigned INT4 codes 0..15, eight per uint32 in the WQ_INT4X8
+ *            nibble order.
+ * WQ_BF16Z   one uint32 per group of an asymmetric INT4 tensor: the bf16
+ *            scale in bits 0..15, the zero-point (0..15) in bits 16..23, the
+ *            rest zero.
  */
 #ifndef WQ_H
 #define WQ_H
@@ -51,7 +56,9 @@ typedef enum {
   WQ_E4M3 = 2,
   WQ_E2M1X2 = 3,
   WQ_E8M0 = 4,
-  WQ_INT4X8 = 5
+  WQ_INT4X8 = 5,
+  WQ_UINT4X8 = 6,
+  WQ_BF16Z = 7
 } wq_dtype;
 
 /* Human-readable name of a status code (static storage, never NULL). */
@@ -192,6 +199,27 @@ wq_status quantize_int4(const void* w, int w_dtype, int64_t rows, int64_t cols,
                         int32_t group, uint32_t* packed, uint16_t* scales, void* stream);
 
 /*
+ * quantize_int4_asym -- fp32/bf16 weights -> asymmetric INT4, x = s * (q - z).
+ *
+ * "Numerics: FP32 to INT4, and why bf16 won": the affine map with a float
+ * scale s and an integer zero-point z (z != 0 covers a range not centred on
+ * zero for one extra subtraction in the dequantization, (q - z) * s); the
+ * all-zero-group policy s = 1; groups of 32 to 128 along K.  Per group, over a
+ * range that contains 0: lo = min(min x, 0), hi = max(max x, 0),
+ * s = bf16(RN_f32(RN_f32(hi - lo) / 15)) (1 if zero),
+ * z = clamp(rint(RN_f32(-lo / s)), 0, 15), q = clamp(rint(RN_f32(x / s)) + z, 0, 15).
+ *
+ * w          rows x cols (N x K), dtype w_dtype (WQ_F32 or WQ_BF16).
+ * group      32, 64 or 128; cols % group == 0.
+ * packed     rows x cols/8 uint32 (output, WQ_UINT4X8).
+ * scalezero  rows x cols/group uint32 (output, WQ_BF16Z).
+ * Groups holding a non-finite value, or whose range overflows fp32, are
+ * outside the contract.
+ */
+wq_status quantize_int4_asym(const void* w, int w_dtype, int64_t rows, int64_t cols,
+                             int32_t group, uint32_t* packed, uint32_t* scalezero, void* stream);
+
+/*
  * wq_dequant -- packed weights + scales -> the bf16 operand the matmul uses.
  *
  * "Your 3090 Isn't Missing Anything for FP8/NVFP4 Weight-Only Inference",
@@ -201,6 +229,8 @@ wq_status quantize_int4(const void* w, int w_dtype, int64_t rows, int64_t cols,
  *       rounding of the exact product.
  *   w_dtype WQ_E2M1X2 + s_dtype WQ_E8M0  (group 16/32): bf16(v * 2^(c-127)),
  *       exact; scale code 255 (E8M0 NaN) is outside the contract.
+ *   w_dtype WQ_UINT4X8 + s_dtype WQ_BF16Z  (group 32/64/128): bf16((q - z) * s),
+ *       one rounding of the exact product; s in (0, 2^120], z <= 15.
  *   w_dtype WQ_E2M1X2 + s_dtype WQ_E4M3  (group 16, NVFP4): v * e4m3 value,
  *       exact (every such product is a bf16 number); the per-tensor scale is
  *       not applied (it is wq_gemm's alpha).  NaN scale codes are outside the
@@ -224,7 +254,9 @@ wq_status wq_dequant(const void* wq, int w_dtype, const void* w_scales, int s_dt
  * sections 2 and 4.1 (bf16 x bf16 multiply after in-register dequantization).
  *
  * Weight/scale pairs:
- *   WQ_INT4X8 + WQ_BF16  group in {32, 64, 128}
+ *   WQ_INT4X8 + WQ_BF16  group in {32, 64, 128}; scales in (0, 2^120]
+ *   WQ_UINT4X8 + WQ_BF16Z  group in {32, 64, 128} (asymmetric INT4, operand
+ *                         bf16((q - z) * s)); scales in (0, 2^120], z <= 15
  *   WQ_E2M1X2 + WQ_E8M0  group 32 (MXFP4)
  *   WQ_E2M1X2 + WQ_E4M3  group 16 (NVFP4; the operand is the exact product of
  *                         the E2M1 and E4M3 values)

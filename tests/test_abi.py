@@ -26,7 +26,7 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("quantize_e4m3", "quantize_mxfp4", "quantize_mx", "quantize_nvfp4", "quantize_int4", "wq_dequant", "wq_gemm",
+    for n in ("quantize_e4m3", "quantize_mxfp4", "quantize_mx", "quantize_nvfp4", "quantize_int4", "quantize_int4_asym", "wq_dequant", "wq_gemm",
               "wq_gemm_workspace_size", "wq_status_string", "wq_moe_route", "wq_w4a8_prepack",
               "wq_w4a8_dequant", "wq_moe_gemm_w4a8"):
         assert n in names
@@ -112,6 +112,16 @@ def test_invalid_arguments_rejected_before_launch(lib):
     assert nv(p, 5, _i64(4), _i64(32), ctypes.c_float(1.0), p, p, None) == 3
     assert nv(q, 0, _i64(4), _i64(32), ctypes.c_float(1.0), p, p, None) == 2
     assert d(p, 3, p, 2, 32, _i64(4), _i64(128), p, None) == 3       # NVFP4 dequant needs group 16
+    assert d(p, 6, p, 1, 128, _i64(4), _i64(128), p, None) == 3      # asymmetric INT4 needs scale-zero words
+    assert d(p, 6, p, 7, 96, _i64(4), _i64(192), p, None) == 3
+    assert gm(*args(1, 16, 128, 6, 1, 128)) == 3
+    assert gm(*args(1, 16, 128, 6, 7, 48)) == 3
+    ia = lib.quantize_int4_asym
+    ia.restype = ctypes.c_int
+    assert ia(p, 0, _i64(4), _i64(128), 96, p, p, None) == 3
+    assert ia(p, 0, _i64(4), _i64(96), 64, p, p, None) == 1
+    assert ia(p, 0, _i64(4), _i64(128), 64, p, None, None) == 1
+    assert ia(q, 0, _i64(4), _i64(128), 64, p, p, None) == 2
     lib.wq_gemm_workspace_size.restype = ctypes.c_size_t
     assert lib.wq_gemm_workspace_size(_i64(1), _i64(16), _i64(128), 5, 128) == 0
 

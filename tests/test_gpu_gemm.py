@@ -116,6 +116,21 @@ def test_decode_full_size(W, decode_weights, kind, M):
     _check(y, xbits, wdeq, chan)
 
 
+@pytest.mark.parametrize("M", [1, 4])
+def test_decode_repeatable_with_cached_weights(W, decode_weights, M):
+    # back-to-back launches over weights that stay in the last-level cache:
+    # every launch must give the same bits (each ring slot is refilled only
+    # after its reads have returned)
+    xbits, _ = decode_inputs(M, seed=40 + M, with_weight=False)
+    args, wdeq, chan = decode_weights["int4"]
+    x = dev_bf16(xbits)
+    banner("decode repeatable M", M)
+    ys = [W.wq_gemm(x, *args, 14336) for _ in range(40)]
+    for y in ys[1:]:
+        assert torch.equal(y, ys[0])
+    _check(ys[0], xbits, wdeq, chan)
+
+
 @pytest.mark.parametrize("kind", ["int4", "mxfp4", "e4m3"])
 @pytest.mark.parametrize("M,N,K", [(300, 520, 512), (17, 256, 256), (512, 512, 1024), (257, 33, 128)])
 def test_gemm_ragged(W, kind, M, N, K):

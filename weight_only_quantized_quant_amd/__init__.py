@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libwq.so")
 
 # dtype enum of the C ABI
-WQ_F32, WQ_BF16, WQ_E4M3, WQ_E2M1X2, WQ_E8M0, WQ_INT4X8 = range(6)
+WQ_F32, WQ_BF16, WQ_E4M3, WQ_E2M1X2, WQ_E8M0, WQ_INT4X8, WQ_UINT4X8, WQ_BF16Z = range(8)
 WQ_OK, WQ_EINVAL, WQ_EALIGN, WQ_EUNSUPPORTED, WQ_EHIP = range(5)
 # E8M0 scale rules of quantize_mx (wq_mx_rule)
 MX_RULES = {"round": 0, "half": 1, "ocp": 2, "floor_div": 3, "ceil_div": 4}
@@ -40,6 +40,7 @@ _SIGS = {
     "quantize_nvfp4": ([_vp, ctypes.c_int, _i64, _i64, ctypes.c_float, _vp, _vp, _vp], ctypes.c_int),
     "quantize_mx": ([_vp, ctypes.c_int, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp], ctypes.c_int),
     "quantize_int4": ([_vp, ctypes.c_int, _i64, _i64, _i32, _vp, _vp, _vp], ctypes.c_int),
+    "quantize_int4_asym": ([_vp, ctypes.c_int, _i64, _i64, _i32, _vp, _vp, _vp], ctypes.c_int),
     "wq_dequant": ([_vp, ctypes.c_int, _vp, ctypes.c_int, _i32, _i64, _i64, _vp, _vp], ctypes.c_int),
     "wq_gemm": ([_vp, _i64, _i64, _i64, _vp, ctypes.c_int, _vp, ctypes.c_int, _i32, ctypes.c_float, _vp, _vp, _sz,
                  _vp], ctypes.c_int),
@@ -179,7 +180,21 @@ def quantize_int4(w: torch.Tensor, group: int = 128, packed=None, scales=None):
     return packed, scales
 
 
-_W_ELEM_BYTES2 = {WQ_INT4X8: 1, WQ_E2M1X2: 1, WQ_E4M3: 2}   # bytes per 2 elements
+def quantize_int4_asym(w: torch.Tensor, group: int = 128, packed=None, scalezero=None):
+    """w: 2-D fp32/bf16 [N, K] -> (packed int32 [N, K/8] holding UINT4X8 words,
+    scale-zero words int32 [N, K/group]: bf16 scale bits | zero-point << 16)."""
+    _dev(w, "w")
+    rows, cols = w.shape
+    if group not in (32, 64, 128) or cols % group:
+        raise ValueError("group must be 32, 64 or 128 and divide cols")
+    packed = _out(packed, (rows, cols // 8), torch.int32, w.device, "packed")
+    scalezero = _out(scalezero, (rows, cols // group), torch.int32, w.device, "scalezero")
+    _check(lib.quantize_int4_asym(w.data_ptr(), _x_dtype(w), rows, cols, group, packed.data_ptr(),
+                                  scalezero.data_ptr(), _stream()), "quantize_int4_asym")
+    return packed, scalezero
+
+
+_W_ELEM_BYTES2 = {WQ_INT4X8: 1, WQ_UINT4X8: 1, WQ_E2M1X2: 1, WQ_E4M3: 2}   # bytes per 2 elements
 
 
 def _check_weight(wq, w_dtype, N, K):
@@ -195,7 +210,7 @@ def _check_scales(sc, s_dtype, N, K, group):
     if sc is None:
         return None
     _dev(sc, "w_scales")
-    per = {WQ_BF16: 2, WQ_E8M0: 1, WQ_E4M3: 1, WQ_F32: 4}[s_dtype]
+    per = {WQ_BF16: 2, WQ_E8M0: 1, WQ_E4M3: 1, WQ_F32: 4, WQ_BF16Z: 4}[s_dtype]
     count = N if s_dtype == WQ_F32 else N * (K // group)
     if sc.numel() * sc.element_size() != count * per:
         raise ValueError("w_scales has the wrong size")

@@ -107,6 +107,23 @@ __device__ __forceinline__ void dq_int4_word(uint32_t w, float s, uint32_t out[4
   for (int j = 0; j < 4; j++) out[j] = pack_bf16x2(e[2 * j], e[2 * j + 1]);
 }
 
+// Unsigned INT4 word (8 codes q in [0, 15]) with scale s and bias b = -z * s:
+// fma(q, s, b) = (q - z) * s exactly (both products have at most 12
+// significant bits for a bf16 s and z <= 15), then one RNE conversion per
+// pair.  Exact for 0 < s <= 2^120.
+__device__ __forceinline__ void dq_uint4_word(uint32_t w, float s, float b, uint32_t out[4]) {
+  const uint32_t ue = w & 0x0F0F0F0Fu;
+  const uint32_t uo = (w >> 4) & 0x0F0F0F0Fu;
+  float e[8];
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    e[2 * j] = __builtin_fmaf((float)((ue >> (8 * j)) & 0xFFu), s, b);
+    e[2 * j + 1] = __builtin_fmaf((float)((uo >> (8 * j)) & 0xFFu), s, b);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; j++) out[j] = pack_bf16x2(e[2 * j], e[2 * j + 1]);
+}
+
 // Same result for any finite s: the magic-constant route above needs
 // 15 * s to stay finite, and for s <= 0 it would give +0 where q * s is -0,
 // so those scales take the direct route (sign-extend each nibble, exact fp32

@@ -21,44 +21,37 @@ using namespace wq;
 namespace {
 
 // W_NV4: E2M1 codes with an E4M3 scale per 16 elements (NVFP4).
-enum { W_INT4 = 0, W_FP4 = 1, W_FP8 = 2, W_NV4 = 3 };
+// W_UINT4: unsigned INT4 codes with a scale-zero word per group (asymmetric).
+enum { W_INT4 = 0, W_FP4 = 1, W_FP8 = 2, W_NV4 = 3, W_UINT4 = 4 };
 
 template <int WDT> struct WTraits;
 template <> struct WTraits<W_INT4> { static constexpr int bits = 4; };
 template <> struct WTraits<W_FP4> { static constexpr int bits = 4; };
 template <> struct WTraits<W_FP8> { static constexpr int bits = 8; };
 template <> struct WTraits<W_NV4> { static constexpr int bits = 4; };
+template <> struct WTraits<W_UINT4> { static constexpr int bits = 4; };
 
 // log2 of the scale group along K (INT4: the caller's group) and bytes per scale
 template <int WDT>
 __host__ __device__ constexpr int gshift_of(int int4_shift) {
-  return WDT == W_INT4 ? int4_shift : WDT == W_NV4 ? 4 : 5;
+  return WDT == W_INT4 || WDT == W_UINT4 ? int4_shift : WDT == W_NV4 ? 4 : 5;
 }
-template <int WDT> constexpr int scale_bytes() { return WDT == W_INT4 ? 2 : 1; }
+template <int WDT> constexpr int scale_bytes() { return WDT == W_INT4 ? 2 : WDT == W_UINT4 ? 4 : 1; }
 
 // Scale operand of one lane's 32-element chunk: one value, or for NVFP4 the
 // values of its two 16-element blocks.
+// For asymmetric INT4: the scale and the bias -z * s.
 struct Sc2 { float lo, hi; };
+struct ScZ { float s, b; };
 template <int WDT> struct ScaleT { using type = float; };
 template <> struct ScaleT<W_NV4> { using type = Sc2; };
+template <> struct ScaleT<W_UINT4> { using type = ScZ; };
 template <int WDT> using scale_t = typename ScaleT<WDT>::type;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   return __builtin_bit_cast(bf16x8_t, u32x4_t{a, b, c, d});
 }
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
-
-// Per-lane scale operand for a 32-element K slice starting at k.
-template <int WDT>
-__device__ __forceinline__ float load_scale(const void* sc, int64_t row, int64_t K, int group, int64_t k) {
-  if constexpr (WDT == W_INT4) {
-    return bf16_to_f32(reinterpret_cast<const uint16_t*>(sc)[row * (K / group) + k / group]);
-  } else if constexpr (WDT == W_FP4) {
-    return e8m0_as_scale(reinterpret_cast<const uint8_t*>(sc)[row * (K / 32) + k / 32]);
-  } else {
-    return 1.0f;
-  }
-}
 
 // Convert one packed 16-byte weight chunk to bf16 MFMA operands.
 // 4-bit: 32 elements -> 4 operands of 8; 8-bit: 16 elements -> 2 operands.
@@ -69,6 +62,13 @@ __device__ __forceinline__ void dequant16(u32x4_t w, scale_t<WDT> s, bf16x8_t ou
     for (int j = 0; j < 4; j++) {
       uint32_t o[4];
       dq_nv4_word(w[j], j < 2 ? s.lo : s.hi, o);
+      out[j] = as_bf16x8(o[0], o[1], o[2], o[3]);
+    }
+  } else if constexpr (WDT == W_UINT4) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      uint32_t o[4];
+      dq_uint4_word(w[j], s.s, s.b, o);
       out[j] = as_bf16x8(o[0], o[1], o[2], o[3]);
     }
   } else if constexpr (WDT == W_INT4) {
@@ -106,6 +106,7 @@ __device__ __forceinline__ uint32_t scale_raw_of(__amdgpu_buffer_rsrc_t r, uint3
   if constexpr (WDT == W_INT4) return __builtin_amdgcn_raw_buffer_load_b16(r, (int)(idx * 2), 0, 0);
   else if constexpr (WDT == W_FP4) return __builtin_amdgcn_raw_buffer_load_b8(r, (int)idx, 0, 0);
   else if constexpr (WDT == W_NV4) return __builtin_amdgcn_raw_buffer_load_b16(r, (int)idx, 0, 0);
+  else if constexpr (WDT == W_UINT4) return __builtin_amdgcn_raw_buffer_load_b32(r, (int)(idx * 4), 0, 0);
   else return 0u;
 }
 template <int WDT>
@@ -115,6 +116,9 @@ __device__ __forceinline__ scale_t<WDT> scale_from_raw(uint32_t raw) {
   else if constexpr (WDT == W_NV4) {
     const uint32_t p = dq_fp8_pair<false>(raw);            // both E4M3 codes, exact in bf16
     return Sc2{bf16_lo(p), bf16_hi(p)};
+  } else if constexpr (WDT == W_UINT4) {
+    const float s = bf16_lo(raw);
+    return ScZ{s, -(float)((raw >> 16) & 0xFFu) * s};
   } else return 1.0f;
 }
 template <int WDT>
@@ -349,6 +353,8 @@ __global__ __launch_bounds__(512) void k_gemm8(const uint16_t* __restrict__ x, i
     } else if constexpr (WDT == W_NV4) {
       // the two blocks of the lane's 32 elements: an even byte offset
       return *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(sc) + srow[j] * (K >> 4) + kk);
+    } else if constexpr (WDT == W_UINT4) {
+      return reinterpret_cast<const uint32_t*>(sc)[srow[j] * (K >> gs) + kk];
     } else {
       return 0u;
     }
@@ -398,6 +404,7 @@ __global__ __launch_bounds__(512) void k_gemm8(const uint16_t* __restrict__ x, i
         uint32_t o[4];
         if constexpr (WDT == W_INT4) dq_int4_word(wd, cs[j], o);
         else if constexpr (WDT == W_NV4) dq_nv4_word(wd, q < 2 ? cs[j].lo : cs[j].hi, o);
+        else if constexpr (WDT == W_UINT4) dq_uint4_word(wd, cs[j].s, cs[j].b, o);
         else dq_fp4_word(wd, cs[j], o);
         out[q][j] = as_bf16x8(o[0], o[1], o[2], o[3]);
       } else {
@@ -488,8 +495,9 @@ __global__ __launch_bounds__(512) void k_gemm8(const uint16_t* __restrict__ x, i
 // A workgroup of 4 waves owns 16 output columns; wave w owns the K-slice of
 // SPW steps [w*SPW, (w+1)*SPW).  Packed weights never occupy VGPRs while in
 // flight: each step's 16 rows x 64 bytes (1 KB) are fetched by direct-to-LDS
-// buffer loads into one of R ring slots of the wave, so many steps of every
-// wave are outstanding at once.  Lane l fetches, and later reads back, the 16
+// buffer loads R steps ahead into a ring of R + 1 slots of the wave, so many
+// steps of every wave are outstanding at once; the extra slot lets each step
+// refill the slot the previous step read.  Lane l fetches, and later reads back, the 16
 // bytes it feeds to the MFMA (row l % 16, K offset 32 or 16 elements times
 // l / 16), so the LDS ring needs no cross-lane synchronisation.  The x rows of
 // the slice are fetched the same way once.  MFMA rows >= M read row 0 of x;
@@ -511,6 +519,10 @@ hipError_t allow_lds(size_t bytes) {
   return f;
 }
 
+// Ring slots of the LDS ring: one more than the prefetch depth R, so that a
+// refill never targets the slot the current step reads.
+__host__ __device__ constexpr int ring_slots(int spw, int r) { return r < spw ? r + 1 : r; }
+
 template <int WDT, int SPW, int R, int NW>
 __global__ __launch_bounds__(64 * NW) void k_gemv_ring(const uint16_t* __restrict__ x, int M, int64_t N, int64_t K,
                                                   const uint8_t* __restrict__ w, const void* __restrict__ sc,
@@ -523,6 +535,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_ring(const uint16_t* __restric
   constexpr int BPE2 = WTraits<WDT>::bits == 4 ? 1 : 2;
   constexpr int XROW = KSL * 2;                               // bytes of one x row of the slice
   static_assert(R <= SPW, "ring larger than the slice");
+  constexpr int NS = ring_slots(SPW, R);
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -542,9 +555,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_ring(const uint16_t* __restric
   // per-wave LDS: ring | M x rows | scales of the slice (16 rows, row stride srs)
   const uint32_t srs = sbrow < 16 ? 16 : sbrow;
   const int sbytes = WDT == W_FP8 ? 0 : 16 * (int)srs;
-  const int wstride = R * 1024 + M * XROW + ((sbytes + 15) & ~15);
+  const int wstride = NS * 1024 + M * XROW + ((sbytes + 15) & ~15);
   uint8_t* ring = smem + wave * wstride;
-  uint8_t* xl = ring + R * 1024;
+  uint8_t* xl = ring + NS * 1024;
   uint8_t* sl = xl + M * XROW;
 
   // 1) scales of the slice.  When a row of the slice holds >= 16 bytes of
@@ -585,7 +598,8 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_ring(const uint16_t* __restric
   const int xr = nl < M ? nl : 0;
 #pragma unroll
   for (int c = 0; c < SPW; c++) {
-    // weight loads issued after step c's: min(R-1, SPW-1-c) (refills are issued in step order)
+    // weight loads issued after step c's: min(R-1, SPW-1-c) (each step issues its
+    // refill after this wait)
     if (c + R - 1 < SPW) wait_vm<R - 1>();
     else {
       switch (SPW - 1 - c) {
@@ -599,7 +613,14 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_ring(const uint16_t* __restric
         default: wait_vm<0>(); break;
       }
     }
-    const u32x4_t wv = *reinterpret_cast<const u32x4_t*>(ring + (c % R) * 1024 + lane * 16);
+    if (c + R < SPW) {
+      // step c + R goes to the slot step c - 1 read: that read returned before
+      // step c - 1's conversion, and nothing may be scheduled across the
+      // barrier (a DMA write is not ordered after an earlier LDS read)
+      __builtin_amdgcn_sched_barrier(0);
+      lds_dma16(rw, ring + ((c + R) % NS) * 1024, wlane + (c + R) * KSTEP * BPE2 / 2);
+    }
+    const u32x4_t wv = *reinterpret_cast<const u32x4_t*>(ring + (c % NS) * 1024 + lane * 16);
     scale_t<WDT> scv{};
     if constexpr (WDT == W_INT4) {
       const uint32_t gi = (uint32_t)(c * KSTEP + EPL * g) >> gs;
@@ -610,6 +631,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_ring(const uint16_t* __restric
     } else if constexpr (WDT == W_NV4) {
       const uint32_t gi = (uint32_t)(c * KSTEP + EPL * g) >> 4;
       scv = scale_from_raw<WDT>(sdma ? (uint32_t)*reinterpret_cast<const uint16_t*>(sl + nl * srs + gi) : svr[c]);
+    } else if constexpr (WDT == W_UINT4) {
+      const uint32_t gi = (uint32_t)(c * KSTEP + EPL * g) >> gs;
+      scv = scale_from_raw<WDT>(sdma ? *reinterpret_cast<const uint32_t*>(sl + nl * srs + 4 * gi) : svr[c]);
     }
     bf16x8_t xa[MF];
 #pragma unroll
@@ -617,8 +641,6 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_ring(const uint16_t* __restric
       xa[j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(xl + xr * XROW + (c * KSTEP + EPL * g + 8 * j) * 2));
     bf16x8_t b[4];
     dequant16<WDT>(wv, scv, b);
-    // the slot's bytes are consumed (in registers): refill it with step c + R
-    if (c + R < SPW) lds_dma16(rw, ring + (c % R) * 1024, wlane + (c + R) * KSTEP * BPE2 / 2);
 #pragma unroll
     for (int j = 0; j < MF; j++) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[j], b[j], acc, 0, 0, 0);
   }
@@ -815,7 +837,9 @@ wq_status ring_go(int64_t M, const uint16_t* x, int64_t N, int64_t K, const uint
   const int sbrow = (KSL >> gs) * scale_bytes<WDT>();
   const int sbytes = WDT == W_FP8 ? 0 : 16 * (sbrow < 16 ? 16 : sbrow);
   const unsigned grid = (unsigned)((N + 15) / 16);
-  auto lds_for = [&](int r) { return (size_t)RING_NW * (r * 1024 + M * KSL * 2 + ((sbytes + 15) & ~15)); };
+  auto lds_for = [&](int r) {
+    return (size_t)RING_NW * (ring_slots(SPW, r) * 1024 + M * KSL * 2 + ((sbytes + 15) & ~15));
+  };
   // 4 resident 4-wave workgroups per CU need <= 40 KB each; trade ring depth for it
   const size_t budget = (size_t)160 * 1024 * RING_NW / 16;
   if (R0 >= 7 && lds_for(R0) > budget && lds_for(R0 - 1) <= budget) {
@@ -911,6 +935,7 @@ wq_status wq_gemm(const void* x_bf16, int64_t M, int64_t N, int64_t K, const voi
   if (w_dtype == WQ_INT4X8 && s_dtype == WQ_BF16 && (group == 32 || group == 64 || group == 128)) wdt = W_INT4;
   else if (w_dtype == WQ_E2M1X2 && s_dtype == WQ_E8M0 && group == 32) wdt = W_FP4;
   else if (w_dtype == WQ_E2M1X2 && s_dtype == WQ_E4M3 && group == 16) wdt = W_NV4;
+  else if (w_dtype == WQ_UINT4X8 && s_dtype == WQ_BF16Z && (group == 32 || group == 64 || group == 128)) wdt = W_UINT4;
   else if (w_dtype == WQ_E4M3 && s_dtype == WQ_F32 && group == K) wdt = W_FP8;
   else return WQ_EUNSUPPORTED;
   if (M > 16 && (int64_t)((M + 255) / 256) * ((N + 255) / 256) > 0x7FFFFFFF) return WQ_EINVAL;   // prefill tiles
@@ -924,6 +949,7 @@ wq_status wq_gemm(const void* x_bf16, int64_t M, int64_t N, int64_t K, const voi
       case W_INT4: return launch_gemv<W_INT4>(x, M, N, K, w, w_scales, group, ch, alpha, y, s);
       case W_FP4: return launch_gemv<W_FP4>(x, M, N, K, w, w_scales, group, ch, alpha, y, s);
       case W_NV4: return launch_gemv<W_NV4>(x, M, N, K, w, w_scales, group, ch, alpha, y, s);
+      case W_UINT4: return launch_gemv<W_UINT4>(x, M, N, K, w, w_scales, group, ch, alpha, y, s);
       default: return launch_gemv<W_FP8>(x, M, N, K, w, w_scales, group, ch, alpha, y, s);
     }
   }
@@ -931,6 +957,7 @@ wq_status wq_gemm(const void* x_bf16, int64_t M, int64_t N, int64_t K, const voi
     case W_INT4: return launch_gemm<W_INT4>(x, M, N, K, w, w_scales, group, ch, alpha, y, s);
     case W_FP4: return launch_gemm<W_FP4>(x, M, N, K, w, w_scales, group, ch, alpha, y, s);
     case W_NV4: return launch_gemm<W_NV4>(x, M, N, K, w, w_scales, group, ch, alpha, y, s);
+    case W_UINT4: return launch_gemm<W_UINT4>(x, M, N, K, w, w_scales, group, ch, alpha, y, s);
     default: return launch_gemm<W_FP8>(x, M, N, K, w, w_scales, group, ch, alpha, y, s);
   }
 }

@@ -1,5 +1,6 @@
 // Block-scaled quantizers (fp32/bf16 -> E4M3, MXFP4, MX with a choice of scale
-// rule and E2M1 or E4M3 elements, NVFP4, INT4) and the dequantizer
+// rule and E2M1 or E4M3 elements, NVFP4, symmetric and asymmetric INT4) and
+// the dequantizer
 // entry point, for gfx950.  Memory-bound: every thread moves 16-byte vectors;
 // block maxima are reduced across the lanes that share a block with xor
 // shuffles.
@@ -356,6 +357,61 @@ __global__ __launch_bounds__(kThreads) void k_dq_fp8(const u32x2_t* __restrict__
   *reinterpret_cast<u32x4_t*>(out + t * 8) = o;
 }
 
+// ---------------------------------------------------------------------------
+// Asymmetric INT4: 16 elements per thread, group/16 lanes per group.  Range
+// [min(min x, 0), max(max x, 0)], s = bf16(RN(RN(hi - lo) / 15)) (1 if zero),
+// z = clamp(rint(RN(-lo / s)), 0, 15), q = clamp(rint(RN(x / s)) + z, 0, 15);
+// one word per group holds the scale bits (low half) and z (bits 16..23).
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_int4_asym(const void* __restrict__ x, int64_t nchunks,
+                                                       int lanes_per_group, uint32_t* __restrict__ packed,
+                                                       uint32_t* __restrict__ scalezero) {
+  const int64_t t0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const bool valid = t0 < nchunks;
+  const int64_t t = valid ? t0 : nchunks - 1;
+  float v[16];
+  load8<BF16>(x, t * 16, v);
+  load8<BF16>(x, t * 16 + 8, v + 8);
+  float hi = 0.0f, nlo = 0.0f;                 // max(x, 0) and max(-x, 0)
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    hi = __builtin_fmaxf(hi, v[i]);
+    nlo = __builtin_fmaxf(nlo, -v[i]);
+  }
+  hi = group_max(hi, lanes_per_group);
+  nlo = group_max(nlo, lanes_per_group);
+  uint32_t sb = f32_to_bf16_bits((hi + nlo) / 15.0f);   // hi - lo with lo = -nlo
+  if ((sb & 0x7FFFu) == 0u) sb = 0x3F80u;
+  const float s = bf16_to_f32(sb);
+  const float z = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(nlo / s), 0.0f), 15.0f);
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    float q = __builtin_rintf(v[i] / s) + z;
+    q = __builtin_fminf(__builtin_fmaxf(q, 0.0f), 15.0f);
+    w[i >> 3] |= ((uint32_t)q) << (4 * (i & 7));
+  }
+  if (valid) {
+    *reinterpret_cast<u32x2_t*>(packed + t * 2) = u32x2_t{w[0], w[1]};
+    if ((threadIdx.x & (lanes_per_group - 1)) == 0) scalezero[t / lanes_per_group] = sb | ((uint32_t)z << 16);
+  }
+}
+
+// (q - z) * s of a word of unsigned codes, from one scale-zero word per group.
+__global__ __launch_bounds__(kThreads) void k_dq_uint4(const uint32_t* __restrict__ packed,
+                                                      const uint32_t* __restrict__ scalezero, int64_t nchunks,
+                                                      int64_t K, int group, uint16_t* __restrict__ out) {
+  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (t >= nchunks) return;
+  const int64_t e = t * 8, n = e / K, k = e % K;
+  const uint32_t sz = scalezero[n * (K / group) + k / group];
+  const float s = bf16_to_f32(sz & 0xFFFFu);
+  uint32_t o[4];
+  dq_uint4_word(packed[t], s, -(float)((sz >> 16) & 0xFFu) * s, o);
+  *reinterpret_cast<u32x4_t*>(out + e) = u32x4_t{o[0], o[1], o[2], o[3]};
+}
+
 inline unsigned grid_for(int64_t n) { return (unsigned)((n + kThreads - 1) / kThreads); }
 
 }  // namespace
@@ -459,6 +515,21 @@ wq_status quantize_int4(const void* w, int w_dtype, int64_t rows, int64_t cols, 
   return wq_launch_status();
 }
 
+wq_status quantize_int4_asym(const void* w, int w_dtype, int64_t rows, int64_t cols, int32_t group,
+                             uint32_t* packed, uint32_t* scalezero, void* stream) {
+  if (!w || !packed || !scalezero || rows <= 0 || cols <= 0) return WQ_EINVAL;
+  if (w_dtype != WQ_F32 && w_dtype != WQ_BF16) return WQ_EUNSUPPORTED;
+  if (group != 32 && group != 64 && group != 128) return WQ_EUNSUPPORTED;
+  if (cols % group || !wq_numel_ok(rows, cols)) return WQ_EINVAL;
+  if (!wq_aligned(w) || !wq_aligned(packed) || !wq_aligned(scalezero)) return WQ_EALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t nch = rows * cols / 16;
+  const int lpg = group / 16;
+  if (w_dtype == WQ_BF16) k_int4_asym<true><<<grid_for(nch), kThreads, 0, s>>>(w, nch, lpg, packed, scalezero);
+  else k_int4_asym<false><<<grid_for(nch), kThreads, 0, s>>>(w, nch, lpg, packed, scalezero);
+  return wq_launch_status();
+}
+
 wq_status wq_dequant(const void* wqp, int w_dtype, const void* w_scales, int s_dtype, int32_t group, int64_t N,
                      int64_t K, uint16_t* w_bf16, void* stream) {
   if (!wqp || !w_bf16 || N <= 0 || K <= 0 || K % 32 || !wq_numel_ok(N, K)) return WQ_EINVAL;
@@ -471,6 +542,14 @@ wq_status wq_dequant(const void* wqp, int w_dtype, const void* w_scales, int s_d
     if (K % group) return WQ_EINVAL;
     k_dq_int4<<<grid_for(nch), kThreads, 0, s>>>((const uint32_t*)wqp, (const uint16_t*)w_scales, nch, K, group,
                                                   w_bf16);
+    return wq_launch_status();
+  }
+  if (w_dtype == WQ_UINT4X8) {
+    if (s_dtype != WQ_BF16Z || (group != 32 && group != 64 && group != 128)) return WQ_EUNSUPPORTED;
+    if (!w_scales) return WQ_EINVAL;
+    if (K % group) return WQ_EINVAL;
+    k_dq_uint4<<<grid_for(nch), kThreads, 0, s>>>((const uint32_t*)wqp, (const uint32_t*)w_scales, nch, K, group,
+                                                   w_bf16);
     return wq_launch_status();
   }
   if (w_dtype == WQ_E2M1X2 && s_dtype == WQ_E4M3) {
