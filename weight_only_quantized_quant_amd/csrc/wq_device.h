@@ -81,14 +81,30 @@ __device__ __forceinline__ uint32_t e8m0_code(float vmax) {
   return be > 2u ? be - 2u : 0u;
 }
 
+// Bytes ue (codes of elements 0, 2, 4, 6) and uo (1, 3, 5, 7), each in [0, 15]:
+// read as E4M3 codes they are u * 2^-9 exactly (codes 0..7 are the subnormals
+// u/8 * 2^-6, codes 8..15 the binade (1 + (u-8)/8) * 2^-6), so one scaled
+// conversion with scale 2^9 turns two of them into exact floats.  Then
+// fma(u, s, b) and one RNE conversion per pair.
+__device__ __forceinline__ void dq_u4_bytes(uint32_t ue, uint32_t uo, float s, float b, uint32_t out[4]) {
+  const auto e01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ue, 512.0f, false);
+  const auto e23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ue, 512.0f, true);
+  const auto o01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(uo, 512.0f, false);
+  const auto o23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(uo, 512.0f, true);
+  out[0] = pack_bf16x2(__builtin_fmaf(e01[0], s, b), __builtin_fmaf(o01[0], s, b));
+  out[1] = pack_bf16x2(__builtin_fmaf(e01[1], s, b), __builtin_fmaf(o01[1], s, b));
+  out[2] = pack_bf16x2(__builtin_fmaf(e23[0], s, b), __builtin_fmaf(o23[0], s, b));
+  out[3] = pack_bf16x2(__builtin_fmaf(e23[1], s, b), __builtin_fmaf(o23[1], s, b));
+}
+
 // INT4 dequantization of one packed word (8 two's-complement nibbles) with
 // bf16-valued group scale s: out[i] holds bf16(q_2i * s), bf16(q_2i+1 * s).
 //
 // Two v_bitop3_b32 split the word into bytes holding u = n ^ 8 = q + 8 (the
 // offset-binary nibble): ((w & 0x0F0F0F0F) ^ 0x08080808) for the even
-// nibbles, the same on w >> 4 for the odd ones.  v_cvt_f32_ubyte{0..3} turn a
-// byte into an exact float, fma(u, s, -8 s) = (u - 8) * s = q * s is exact
-// (-8 s is exact and q * s has at most 11 significant bits), and one RNE
+// nibbles, the same on w >> 4 for the odd ones.  dq_u4_bytes turns the bytes
+// into exact floats two at a time, fma(u, s, -8 s) = (u - 8) * s = q * s is
+// exact (-8 s is exact and q * s has at most 11 significant bits), and one RNE
 // conversion per pair makes bf16(q * s).  Exact in value for 0 < s <= 2^120;
 // for s <= 0 a zero product may come out as +0 instead of -0.
 __device__ __forceinline__ void dq_int4_word(uint32_t w, float s, uint32_t out[4]) {
@@ -96,15 +112,7 @@ __device__ __forceinline__ void dq_int4_word(uint32_t w, float s, uint32_t out[4
   constexpr uint8_t AND_XOR = (uint8_t)((0xF0 & 0xCC) ^ 0xAA);
   const uint32_t ue = __builtin_amdgcn_bitop3_b32(w, 0x0F0F0F0Fu, 0x08080808u, AND_XOR);
   const uint32_t uo = __builtin_amdgcn_bitop3_b32(w >> 4, 0x0F0F0F0Fu, 0x08080808u, AND_XOR);
-  const float b = s * -8.0f;
-  float e[8];
-#pragma unroll
-  for (int j = 0; j < 4; j++) {
-    e[2 * j] = __builtin_fmaf((float)((ue >> (8 * j)) & 0xFFu), s, b);
-    e[2 * j + 1] = __builtin_fmaf((float)((uo >> (8 * j)) & 0xFFu), s, b);
-  }
-#pragma unroll
-  for (int j = 0; j < 4; j++) out[j] = pack_bf16x2(e[2 * j], e[2 * j + 1]);
+  dq_u4_bytes(ue, uo, s, s * -8.0f, out);
 }
 
 // Unsigned INT4 word (8 codes q in [0, 15]) with scale s and bias b = -z * s:
@@ -112,16 +120,7 @@ __device__ __forceinline__ void dq_int4_word(uint32_t w, float s, uint32_t out[4
 // significant bits for a bf16 s and z <= 15), then one RNE conversion per
 // pair.  Exact for 0 < s <= 2^120.
 __device__ __forceinline__ void dq_uint4_word(uint32_t w, float s, float b, uint32_t out[4]) {
-  const uint32_t ue = w & 0x0F0F0F0Fu;
-  const uint32_t uo = (w >> 4) & 0x0F0F0F0Fu;
-  float e[8];
-#pragma unroll
-  for (int j = 0; j < 4; j++) {
-    e[2 * j] = __builtin_fmaf((float)((ue >> (8 * j)) & 0xFFu), s, b);
-    e[2 * j + 1] = __builtin_fmaf((float)((uo >> (8 * j)) & 0xFFu), s, b);
-  }
-#pragma unroll
-  for (int j = 0; j < 4; j++) out[j] = pack_bf16x2(e[2 * j], e[2 * j + 1]);
+  dq_u4_bytes(w & 0x0F0F0F0Fu, (w >> 4) & 0x0F0F0F0Fu, s, b, out);
 }
 
 // Same result for any finite s: the magic-constant route above needs
