@@ -32,6 +32,8 @@ int4      symmetric INT4 group quantizer with bf16 scales
 int4_asym asymmetric INT4: unsigned codes, bf16 group scale, integer zero-point
 dequant   packed weights + scales -> bf16 operands
 gemm      fp64 reference matmul and the acceptance bound
+w8a8      W8A8 FP8: static per-tensor activation quantizer, 128 x 128 weight
+          blocks, the block-scaled fp32 reference
 w4a8      MoE routing, W4A8 scale recipe, INT4 -> E4M3 lookup table, grouped GEMM
 
 Parity status: every function is pinned by CPU tests against values the pages
