@@ -18,13 +18,14 @@ and `secondary` measurements: decode at M = 4 and 16, W8A16, asymmetric INT4
 decode at M = 1, NVFP4 decode at M = 1 and 16, prefill MXFP4 and NVFP4 at M = 8192 (TFLOP/s), the activation
 quantizers at 4096 x 7168 (E4M3 per 128, MXFP4 per 16, MXFP8 per 32 under two
 E8M0 rules, and the share of blocks whose maximum clips under each rule), the
-MXFP4 weight quantizer, the W4A8 mixture-of-experts grouped GEMMs (gate/up and
+MXFP4 weight quantizer, the W8A8 FP8 GEMM at the prefill shape (block-scaled
+and per-token x per-channel), the W4A8 mixture-of-experts grouped GEMMs (gate/up and
 down, with routing, token quantization and prepack), a streaming copy and
 torch.matmul (hipBLASLt) at the prefill shape as secondary denominators.
 
 --only CASE runs a single case without the full summary (for rocprofv3):
 decode (the same graph-timed steps as the headline, prints one short JSON
-line), decode_w8, decode_nvfp4, decode_asym, prefill, prefill_nvfp4, quant_e4m3, quant_mxfp4, quant_mxfp8, wquant_mxfp4, copy,
+line), decode_w8, decode_nvfp4, decode_asym, prefill, prefill_nvfp4, w8a8_block, w8a8_channel, quant_e4m3, quant_mxfp4, quant_mxfp8, wquant_mxfp4, copy,
 moe_gate_up, moe_down.
 """
 from __future__ import annotations
@@ -215,6 +216,35 @@ class Prefill:
         self.W.wq_gemm(self.x, self.codes, wdt, self.sc, sdt, grp, self.N, y=self.y, alpha=self.alpha)
 
 
+class W8A8:
+    """x[8192, 4096] . W[14336, 4096]^T in W8A8 FP8: "block" = per-token
+    1x128-group activation scales and 128x128 weight blocks (scales folded in
+    per K block); "channel" = per-token activation and per-channel weight
+    scales (applied to the finished sums).  Quantized on the GPU."""
+
+    def __init__(self, torch, W, mode, M=8192, K=4096, N=14336):
+        from synthetic import prefill_inputs
+        self.W, self.M, self.K, self.N, self.mode = W, M, K, N, mode
+        xbits, Wf = prefill_inputs(0, M=M, K=K, N=N)
+        x = dev_bf16(torch, xbits)
+        wdev = torch.from_numpy(Wf).cuda()
+        if mode == "block":
+            self.a, sa = W.quantize_e4m3(x, 128)
+            self.b, sb = W.quantize_e4m3_block2d(wdev)
+            self.args = (sa.reshape(-1), K // 128, 1, sb.reshape(-1), K // 128, 1, 128)
+        else:
+            self.a, sa = W.quantize_e4m3(x, -1)
+            self.b, sb = W.quantize_e4m3(wdev, -1)
+            self.args = (sa.reshape(-1), 1, 0, sb.reshape(-1), 1, 0, 1)
+        del wdev, x
+        self.y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        self.flops = 2.0 * M * N * K
+
+    def launch(self, i):
+        sa, as_m, as_k, sb, bs_n, bs_k, gn = self.args
+        self.W.wq_gemm_w8a8(self.a, sa, as_m, as_k, self.b, sb, bs_n, bs_k, gn, y=self.y)
+
+
 class ActQuant:
     """4096 x 7168 bf16 -> E4M3 per 1x128 (fp32 scales), MXFP4 per 16 (E8M0) or
     MXFP8 (E4M3 elements, E8M0 per 32) under a chosen scale rule."""
@@ -374,13 +404,15 @@ def main():
         mk = {"decode_w8": lambda: Decode(torch, W, 1, "e4m3"), "decode_nvfp4": lambda: Decode(torch, W, 1, "nvfp4"),
               "decode_asym": lambda: Decode(torch, W, 1, "int4_asym"),
               "prefill_nvfp4": lambda: Prefill(torch, W, kind="nvfp4"),
+              "w8a8_block": lambda: W8A8(torch, W, "block"), "w8a8_channel": lambda: W8A8(torch, W, "channel"),
               "prefill": lambda: Prefill(torch, W), "quant_e4m3": lambda: ActQuant(torch, W, "e4m3"),
               "quant_mxfp4": lambda: ActQuant(torch, W, "mxfp4"), "copy": lambda: Copy(torch),
               "quant_mxfp8": lambda: ActQuant(torch, W, "mxfp8"),
               "wquant_mxfp4": lambda: WeightQuant(torch, W),
               "moe_gate_up": lambda: MoeW4A8(torch, W, "gate_up"), "moe_down": lambda: MoeW4A8(torch, W, "down")}[case]
         obj = mk()
-        reps = args.reps or (10 if case in ("prefill", "prefill_nvfp4", "moe_gate_up", "moe_down") else 100)
+        reps = args.reps or (10 if case in ("prefill", "prefill_nvfp4", "moe_gate_up", "moe_down", "w8a8_block",
+                                            "w8a8_channel") else 100)
         for i in range(reps):
             obj.launch(i)
         torch.cuda.synchronize()
@@ -444,6 +476,14 @@ def main():
                                         "ms": round(t, 3)}
     del pf
     torch.cuda.empty_cache()
+    for mode in ("block", "channel"):
+        g8 = W8A8(torch, W, mode)
+        t = time_eager(torch, g8.launch, 10)
+        tf = g8.flops / (t * 1e-3) / 1e12
+        secondary[f"w8a8_{mode}_8192x14336x4096"] = {"TFLOP/s": round(tf, 1), "frac_fp8_mfma": round(tf / FP8_PEAK_TFLOPS, 4),
+                                                     "ms": round(t, 3)}
+        del g8
+        torch.cuda.empty_cache()
 
     for kind, rule in (("e4m3", None), ("mxfp4", None), ("mxfp8", "round"), ("mxfp8", "ceil_div")):
         q = ActQuant(torch, W, kind, rule)

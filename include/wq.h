@@ -282,6 +282,68 @@ wq_status wq_gemm(const void* x_bf16, int64_t M, int64_t N, int64_t K,
 size_t wq_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int w_dtype, int32_t group);
 
 /*
+ * W8A8 FP8 path
+ * -------------
+ * Defined by "Numerics: FP32 to INT4, and why bf16 won": the Triton
+ * block-scaled FP8 GEMM of the section on storage and accumulation dtypes
+ * (fp32 accumulator; per K block the fp8 product is scaled by the activation
+ * scale of each row and the weight scale of each column; one narrowing cast at
+ * the store) and the fp8 linear walkthrough (step 2: divide by the scale in
+ * fp32, saturating clamp, conversion; step 3: fp8 x fp8 with both scales
+ * folded in inside the K loop, one cast to bf16).  K blocks are 128 wide.
+ */
+
+/*
+ * quantize_e4m3_static -- per-tensor static E4M3 quantization with a given
+ * scale (the per-tensor cast site FreeToken PR #805 lists):
+ * codes = e4m3(RN_f32(x / scale)), correctly rounded division, saturating at
+ * +-448.
+ * x      rows x cols, dtype x_dtype (WQ_F32 or WQ_BF16); cols % 16 == 0.
+ * scale  DEVICE pointer to one fp32 value > 0 (read by the kernel, so a
+ *        calibrated scale never round-trips through the host).
+ * codes  rows x cols bytes (output).
+ * Non-finite inputs and non-positive scales are outside the contract.
+ */
+wq_status quantize_e4m3_static(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                               const float* scale, uint8_t* codes, void* stream);
+
+/*
+ * quantize_e4m3_block2d -- weights -> E4M3 with one fp32 scale per 128 x 128
+ * block: s = RN_f32(amax / 448) (1 if zero), codes e4m3(RN_f32(w / s)).
+ * w       rows x cols (N x K), dtype w_dtype (WQ_F32 or WQ_BF16); cols % 128 == 0;
+ *         a partial last row block uses the rows it has.
+ * codes   rows x cols bytes (output).
+ * scales  ceil(rows/128) x cols/128 fp32 (output).
+ */
+wq_status quantize_e4m3_block2d(const void* w, int w_dtype, int64_t rows, int64_t cols,
+                                uint8_t* codes, float* scales, void* stream);
+
+/*
+ * wq_gemm_w8a8 -- y[M,N] = sum over K blocks kb of a_s(m,kb) b_s(n,kb) *
+ * sum_{k in kb} a[m,k] b[n,k], E4M3 operands, fp32 accumulation, one bf16
+ * rounding.
+ *
+ * a        M x K E4M3 activations.  a_scale: fp32, the scale of (m, kb) is
+ *          a_scale[m * as_m + kb * as_k] (per tensor: 0, 0; per token: 1, 0;
+ *          per token and 128-wide group: K/128, 1).
+ * b        N x K E4M3 weights.  b_scale: fp32, the scale of (n, kb) is
+ *          b_scale[(n / group_n) * bs_n + kb * bs_k]; group_n 128 (128 x 128
+ *          blocks: bs_n = K/128, bs_k = 1; or one scale per 128 channels) or 1
+ *          (per channel, bs_k must be 0); per tensor: bs_n = bs_k = 0.
+ * y        M x N bf16 (output).
+ * K % 128 == 0.  When a scale depends on kb, every K block's partial sums are
+ * scaled before they are added; otherwise the scales multiply the finished
+ * fp32 sums.  Scale arrays must hold every index the strides reach; negative
+ * strides are WQ_EINVAL.  The fp8 matrix cores treat E4M3 subnormal operands
+ * as zero.  Accuracy contract: |y - y_ref| <= 8e-3 |y_ref| + 1e-3 sum_k
+ * |a_k s_a b_k s_b|.
+ */
+wq_status wq_gemm_w8a8(const uint8_t* a, const float* a_scale, int64_t as_m, int64_t as_k,
+                       const uint8_t* b, const float* b_scale, int64_t bs_n, int64_t bs_k,
+                       int32_t group_n, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                       void* stream);
+
+/*
  * W4A8 mixture-of-experts path
  * ----------------------------
  * Defined by "Production-Ready W4A8: vLLM Integration and Quality Recovery

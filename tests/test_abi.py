@@ -28,7 +28,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("quantize_e4m3", "quantize_mxfp4", "quantize_mx", "quantize_nvfp4", "quantize_int4", "quantize_int4_asym", "wq_dequant", "wq_gemm",
               "wq_gemm_workspace_size", "wq_status_string", "wq_moe_route", "wq_w4a8_prepack",
-              "wq_w4a8_dequant", "wq_moe_gemm_w4a8"):
+              "wq_w4a8_dequant", "wq_moe_gemm_w4a8", "quantize_e4m3_static", "quantize_e4m3_block2d",
+              "wq_gemm_w8a8"):
         assert n in names
 
 
@@ -125,6 +126,32 @@ def test_invalid_arguments_rejected_before_launch(lib):
     lib.wq_gemm_workspace_size.restype = ctypes.c_size_t
     assert lib.wq_gemm_workspace_size(_i64(1), _i64(16), _i64(128), 5, 128) == 0
 
+
+
+def test_w8a8_invalid_arguments_rejected_before_launch(lib):
+    p = ctypes.c_void_p(0x1000)
+    q = ctypes.c_void_p(0x1004)          # misaligned for 16-byte data, aligned for fp32 scales
+    st = lib.quantize_e4m3_static
+    st.restype = ctypes.c_int
+    assert st(p, 1, _i64(4), _i64(24), p, p, None) == 1                  # cols % 16
+    assert st(p, 1, _i64(4), _i64(32), None, p, None) == 1               # scale pointer
+    assert st(p, 4, _i64(4), _i64(32), p, p, None) == 3
+    assert st(q, 1, _i64(4), _i64(32), p, p, None) == 2
+    bl = lib.quantize_e4m3_block2d
+    bl.restype = ctypes.c_int
+    assert bl(p, 0, _i64(300), _i64(200), p, p, None) == 1               # cols % 128
+    assert bl(p, 0, _i64(0), _i64(256), p, p, None) == 1
+    assert bl(p, 0, _i64(300), _i64(256), q, p, None) == 2
+    g = lib.wq_gemm_w8a8
+    g.restype = ctypes.c_int
+    args = lambda M, N, K, gn=128, bsk=1, ask=1, a=p: (a, p, _i64(K // 128), _i64(ask), p, p, _i64(K // 128),
+                                                       _i64(bsk), gn, _i64(M), _i64(N), _i64(K), p, None)
+    assert g(*args(16, 256, 200)) == 1                                  # K % 128
+    assert g(*args(0, 256, 256)) == 1
+    assert g(*args(16, 256, 256, gn=64)) == 3                           # block of 128 channels or per channel
+    assert g(*args(16, 256, 256, gn=1, bsk=1)) == 3                     # per-channel scales cannot depend on K
+    assert g(*args(16, 256, 256, ask=-1)) == 1
+    assert g(*args(16, 256, 256, a=q)) == 2
 
 
 def test_moe_invalid_arguments_rejected_before_launch(lib):

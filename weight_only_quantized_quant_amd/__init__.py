@@ -45,6 +45,9 @@ _SIGS = {
     "wq_gemm": ([_vp, _i64, _i64, _i64, _vp, ctypes.c_int, _vp, ctypes.c_int, _i32, ctypes.c_float, _vp, _vp, _sz,
                  _vp], ctypes.c_int),
     "wq_gemm_workspace_size": ([_i64, _i64, _i64, ctypes.c_int, _i32], _sz),
+    "quantize_e4m3_static": ([_vp, ctypes.c_int, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
+    "quantize_e4m3_block2d": ([_vp, ctypes.c_int, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
+    "wq_gemm_w8a8": ([_vp, _vp, _i64, _i64, _vp, _vp, _i64, _i64, _i32, _i64, _i64, _i64, _vp, _vp], ctypes.c_int),
     "wq_moe_route": ([_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "wq_w4a8_prepack": ([_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp], ctypes.c_int),
     "wq_w4a8_dequant": ([_vp, _vp, _i64, _i64, _vp, _vp], ctypes.c_int),
@@ -246,6 +249,57 @@ def wq_gemm(x: torch.Tensor, wq: torch.Tensor, w_dtype: int, w_scales: torch.Ten
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     _check(lib.wq_gemm(x.data_ptr(), M, N, K, wq.data_ptr(), w_dtype, sp, s_dtype, group, float(alpha), y.data_ptr(),
                        ws_ptr, ws_bytes, _stream()), "wq_gemm")
+    return y
+
+
+# ---------------------------------------------------------------------------
+# W8A8 FP8
+# ---------------------------------------------------------------------------
+def quantize_e4m3_static(x: torch.Tensor, scale: torch.Tensor, codes=None):
+    """x: 2-D fp32/bf16; scale: a one-element fp32 device tensor.  Returns E4M3
+    codes uint8 [rows, cols] = e4m3(x / scale)."""
+    _dev(x, "x")
+    _typed(scale, torch.float32, (1,), "scale")
+    rows, cols = x.shape
+    codes = _out(codes, (rows, cols), torch.uint8, x.device, "codes")
+    _check(lib.quantize_e4m3_static(x.data_ptr(), _x_dtype(x), rows, cols, scale.data_ptr(), codes.data_ptr(),
+                                    _stream()), "quantize_e4m3_static")
+    return codes
+
+
+def quantize_e4m3_block2d(w: torch.Tensor, codes=None, scales=None):
+    """w: 2-D fp32/bf16 [N, K] -> (E4M3 codes uint8 [N, K], fp32 scales
+    [ceil(N/128), K/128], one per 128 x 128 block)."""
+    _dev(w, "w")
+    rows, cols = w.shape
+    codes = _out(codes, (rows, cols), torch.uint8, w.device, "codes")
+    scales = _out(scales, ((rows + 127) // 128, cols // 128), torch.float32, w.device, "scales")
+    _check(lib.quantize_e4m3_block2d(w.data_ptr(), _x_dtype(w), rows, cols, codes.data_ptr(), scales.data_ptr(),
+                                     _stream()), "quantize_e4m3_block2d")
+    return codes, scales
+
+
+def wq_gemm_w8a8(a: torch.Tensor, a_scale: torch.Tensor, as_m: int, as_k: int, b: torch.Tensor, b_scale: torch.Tensor,
+                 bs_n: int, bs_k: int, group_n: int, y=None):
+    """y[M, N] (bf16) = sum over 128-wide K blocks kb of a_scale[m*as_m + kb*as_k] *
+    b_scale[(n//group_n)*bs_n + kb*bs_k] * (a[m, kb] . b[n, kb]); a [M, K] and b [N, K]
+    uint8 E4M3 codes, scales fp32 device tensors holding every index the strides reach."""
+    for t, name in ((a, "a"), (b, "b"), (a_scale, "a_scale"), (b_scale, "b_scale")):
+        _dev(t, name)
+    if a.dtype != torch.uint8 or b.dtype != torch.uint8 or a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[1]:
+        raise ValueError("a and b must be 2-D uint8 E4M3 codes with the same K")
+    if a_scale.dtype != torch.float32 or b_scale.dtype != torch.float32:
+        raise ValueError("scales must be float32")
+    M, K = a.shape
+    N = b.shape[0]
+    kb = K // 128 if K % 128 == 0 else 0
+    need_a = (M - 1) * as_m + (kb - 1) * as_k + 1 if kb else 0
+    need_b = ((N - 1) // max(group_n, 1)) * bs_n + (kb - 1) * bs_k + 1 if kb else 0
+    if kb and (a_scale.numel() < need_a or b_scale.numel() < need_b):
+        raise ValueError("a scale array is smaller than its strides reach")
+    y = _out(y, (M, N), torch.bfloat16, a.device, "y")
+    _check(lib.wq_gemm_w8a8(a.data_ptr(), a_scale.data_ptr(), as_m, as_k, b.data_ptr(), b_scale.data_ptr(), bs_n, bs_k,
+                            group_n, M, N, K, y.data_ptr(), _stream()), "wq_gemm_w8a8")
     return y
 
 

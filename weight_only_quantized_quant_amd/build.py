@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libwq.so")
 
-SOURCES = ["wq_quant.hip", "wq_gemm.hip", "wq_moe.hip", "wq_status.cpp"]
+SOURCES = ["wq_quant.hip", "wq_gemm.hip", "wq_moe.hip", "wq_w8a8.hip", "wq_status.cpp"]
 
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32.
 HIP_FLAGS = [
