@@ -523,7 +523,7 @@ hipError_t allow_lds(size_t bytes) {
 // refill never targets the slot the current step reads.
 __host__ __device__ constexpr int ring_slots(int spw, int r) { return r < spw ? r + 1 : r; }
 
-template <int WDT, int SPW, int R, int NW>
+template <int WDT, int SPW, int R, int NW, bool SDMA>
 __global__ __launch_bounds__(64 * NW) void k_gemv_ring(const uint16_t* __restrict__ x, int M, int64_t N, int64_t K,
                                                   const uint8_t* __restrict__ w, const void* __restrict__ sc,
                                                   int group_shift, const float* __restrict__ chscale,
@@ -564,7 +564,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_ring(const uint16_t* __restric
   //    scales (a multiple of 16), they arrive by DMA, 16 bytes per lane; for
   //    thinner slices every lane loads its own per-step scales instead (a 16-byte
   //    window could leave the buffer range at the last row and read as zeros).
-  const bool sdma = sbrow >= 16;
+  constexpr bool sdma = SDMA;                                // sbrow >= 16, decided by the host
   uint32_t svr[SPW];
   if constexpr (WDT != W_FP8) {
     if (sdma) {
@@ -840,17 +840,14 @@ wq_status ring_go(int64_t M, const uint16_t* x, int64_t N, int64_t K, const uint
   auto lds_for = [&](int r) {
     return (size_t)RING_NW * (ring_slots(SPW, r) * 1024 + M * KSL * 2 + ((sbytes + 15) & ~15));
   };
-  // 4 resident 4-wave workgroups per CU need <= 40 KB each; trade ring depth for it
-  const size_t budget = (size_t)160 * 1024 * RING_NW / 16;
-  if (R0 >= 7 && lds_for(R0) > budget && lds_for(R0 - 1) <= budget) {
-    constexpr int R = R0 >= 7 ? R0 - 1 : R0;
-    if (allow_lds<k_gemv_ring<WDT, SPW, R, RING_NW>>(lds_for(R)) != hipSuccess) return WQ_EHIP;
-    k_gemv_ring<WDT, SPW, R, RING_NW><<<grid, 64 * RING_NW, lds_for(R), s>>>(x, (int)M, N, K, w, sc, gshift, ch, alpha,
-                                                                                   y);
+  const size_t lds = lds_for(R0);
+  if (sbrow >= 16) {
+    if (allow_lds<k_gemv_ring<WDT, SPW, R0, RING_NW, true>>(lds) != hipSuccess) return WQ_EHIP;
+    k_gemv_ring<WDT, SPW, R0, RING_NW, true><<<grid, 64 * RING_NW, lds, s>>>(x, (int)M, N, K, w, sc, gshift, ch, alpha, y);
   } else {
-    if (allow_lds<k_gemv_ring<WDT, SPW, R0, RING_NW>>(lds_for(R0)) != hipSuccess) return WQ_EHIP;
-    k_gemv_ring<WDT, SPW, R0, RING_NW><<<grid, 64 * RING_NW, lds_for(R0), s>>>(x, (int)M, N, K, w, sc, gshift, ch, alpha,
-                                                                                    y);
+    if (allow_lds<k_gemv_ring<WDT, SPW, R0, RING_NW, false>>(lds) != hipSuccess) return WQ_EHIP;
+    k_gemv_ring<WDT, SPW, R0, RING_NW, false><<<grid, 64 * RING_NW, lds, s>>>(x, (int)M, N, K, w, sc, gshift, ch, alpha,
+                                                                              y);
   }
   return WQ_OK;
 }
