@@ -828,28 +828,38 @@ wq_status ring16_go(int64_t M, const uint16_t* x, int64_t N, int64_t K, const ui
   }
 }
 
+template <int WDT, int SPW, int R, bool SDMA>
+wq_status ring_launch(int64_t M, const uint16_t* x, int64_t N, int64_t K, const uint8_t* w, const void* sc, int gshift,
+                      const float* ch, float alpha, uint16_t* y, size_t lds, hipStream_t s) {
+  if (allow_lds<k_gemv_ring<WDT, SPW, R, RING_NW, SDMA>>(lds) != hipSuccess) return WQ_EHIP;
+  const unsigned grid = (unsigned)((N + 15) / 16);
+  k_gemv_ring<WDT, SPW, R, RING_NW, SDMA><<<grid, 64 * RING_NW, lds, s>>>(x, (int)M, N, K, w, sc, gshift, ch, alpha, y);
+  return WQ_OK;
+}
+
+// Loads run RING_DEPTH steps ahead for one or two tokens; with 3-4 tokens the
+// steps take longer and a deeper ring keeps more bytes in flight (measured at
+// M = 4: one more step for 4-bit weights, two more for 8-bit; at M = 2 the
+// shallow ring is still faster).
 template <int WDT, int SPW>
 wq_status ring_go(int64_t M, const uint16_t* x, int64_t N, int64_t K, const uint8_t* w, const void* sc, int gshift,
                   const float* ch, float alpha, uint16_t* y, hipStream_t s) {
-  constexpr int R0 = SPW < RING_DEPTH ? SPW : RING_DEPTH;
+  constexpr int R1 = SPW < RING_DEPTH ? SPW : RING_DEPTH;
+  constexpr int RM0 = RING_DEPTH + (WTraits<WDT>::bits == 8 ? 2 : 1);
+  constexpr int RM = SPW < RM0 ? SPW : RM0;
   constexpr int KSL = SPW * (WTraits<WDT>::bits == 4 ? 128 : 64);
   const int gs = gshift_of<WDT>(gshift);
   const int sbrow = (KSL >> gs) * scale_bytes<WDT>();
   const int sbytes = WDT == W_FP8 ? 0 : 16 * (sbrow < 16 ? 16 : sbrow);
-  const unsigned grid = (unsigned)((N + 15) / 16);
-  auto lds_for = [&](int r) {
-    return (size_t)RING_NW * (ring_slots(SPW, r) * 1024 + M * KSL * 2 + ((sbytes + 15) & ~15));
-  };
-  const size_t lds = lds_for(R0);
-  if (sbrow >= 16) {
-    if (allow_lds<k_gemv_ring<WDT, SPW, R0, RING_NW, true>>(lds) != hipSuccess) return WQ_EHIP;
-    k_gemv_ring<WDT, SPW, R0, RING_NW, true><<<grid, 64 * RING_NW, lds, s>>>(x, (int)M, N, K, w, sc, gshift, ch, alpha, y);
-  } else {
-    if (allow_lds<k_gemv_ring<WDT, SPW, R0, RING_NW, false>>(lds) != hipSuccess) return WQ_EHIP;
-    k_gemv_ring<WDT, SPW, R0, RING_NW, false><<<grid, 64 * RING_NW, lds, s>>>(x, (int)M, N, K, w, sc, gshift, ch, alpha,
-                                                                              y);
+  const bool shallow = M <= 2;
+  const int r = shallow ? R1 : RM;
+  const size_t lds = (size_t)RING_NW * (ring_slots(SPW, r) * 1024 + M * KSL * 2 + ((sbytes + 15) & ~15));
+  if (shallow) {
+    return sbrow >= 16 ? ring_launch<WDT, SPW, R1, true>(M, x, N, K, w, sc, gshift, ch, alpha, y, lds, s)
+                       : ring_launch<WDT, SPW, R1, false>(M, x, N, K, w, sc, gshift, ch, alpha, y, lds, s);
   }
-  return WQ_OK;
+  return sbrow >= 16 ? ring_launch<WDT, SPW, RM, true>(M, x, N, K, w, sc, gshift, ch, alpha, y, lds, s)
+                     : ring_launch<WDT, SPW, RM, false>(M, x, N, K, w, sc, gshift, ch, alpha, y, lds, s);
 }
 
 template <int WDT>
