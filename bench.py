@@ -96,18 +96,24 @@ def time_graph(torch, g, launches):
     return a.elapsed_time(b) / launches
 
 
-def time_eager(torch, fn, reps, warm=2):
+def time_eager(torch, fn, reps, warm=3, rounds=3):
+    """Median over `rounds` timed rounds of `reps` eager launches, after `warm`
+    untimed launches (the first launches of a large kernel run before the
+    clocks have settled)."""
     for _ in range(warm):
         fn(0)
     torch.cuda.synchronize()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record()
-    for i in range(reps):
-        fn(i)
-    b.record()
-    b.synchronize()
-    return a.elapsed_time(b) / reps
+    ms = []
+    for _ in range(rounds):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(reps):
+            fn(i)
+        b.record()
+        b.synchronize()
+        ms.append(a.elapsed_time(b) / reps)
+    return sorted(ms)[len(ms) // 2]
 
 
 def kernel_source_hash():

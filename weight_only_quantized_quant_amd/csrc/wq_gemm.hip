@@ -704,7 +704,7 @@ void gemv_nstep(const GemvSplit& sp, const uint16_t* x, int64_t M, int64_t N, in
 // L2 by every workgroup).  A row's 16-byte chunks are XOR-swizzled by the row
 // so that the 16 lanes reading one chunk of 16 rows use distinct banks; rows
 // >= M read as zeros.  Scales come from per-lane loads issued up front.
-template <int WDT, int SPW, int R, int NW>
+template <int WDT, int SPW, int R, int NW, int CT>
 __global__ __launch_bounds__(64 * NW) void k_gemv_ring16(const uint16_t* __restrict__ x, int M, int64_t N,
                                                     int64_t K, const uint8_t* __restrict__ w,
                                                     const void* __restrict__ sc, int group_shift,
@@ -720,16 +720,16 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_ring16(const uint16_t* __restr
   constexpr int XQ = XSLOT / 1024;                            // x DMA instructions per step
   constexpr int RPI = 1024 / XRB;                             // x rows per DMA instruction
   constexpr int CPR = XRB / 16;                               // 16-byte chunks per x row
-  constexpr int VMS = 1 + XQ;                                 // loads per step per lane
-  constexpr int SLOT = 1024 + XSLOT;
+  constexpr int VMS = CT + XQ;                                // loads per step per lane
+  constexpr int SLOT = CT * 1024 + XSLOT;                     // CT weight chunks, then x
   static_assert(R <= SPW && R == 2, "two-deep ring");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nl = lane & 15, g = lane >> 4;
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int64_t n0 = (int64_t)blockIdx.x * 16 * CT;
   const uint32_t rowbytes = (uint32_t)(K * BPE2 / 2);
-  const int64_t nrows = N - n0 < 16 ? N - n0 : 16;
+  const int64_t nrows = N - n0 < 16 * CT ? N - n0 : 16 * CT;
   const int gs = gshift_of<WDT>(group_shift);
   const uint32_t spr = (uint32_t)(K >> gs);
   constexpr int SB = scale_bytes<WDT>();
@@ -740,11 +740,13 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_ring16(const uint16_t* __restr
   const uint32_t kbase = (uint32_t)(wave * KSL);
   uint8_t* ring = smem + wave * (R * SLOT);
 
-  uint32_t svr[SPW];
+  uint32_t svr[SPW][CT];
   if constexpr (WDT != W_FP8) {
 #pragma unroll
     for (int c = 0; c < SPW; c++)
-      svr[c] = scale_raw_of<WDT>(rs, (uint32_t)nl * spr + ((kbase + c * KSTEP + EPL * g) >> gs));
+#pragma unroll
+      for (int t = 0; t < CT; t++)
+        svr[c][t] = scale_raw_of<WDT>(rs, (uint32_t)(16 * t + nl) * spr + ((kbase + c * KSTEP + EPL * g) >> gs));
   }
   const uint32_t wlane = (uint32_t)nl * rowbytes + (kbase + EPL * g) * BPE2 / 2;
   uint32_t xoff[XQ];
@@ -756,50 +758,60 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_ring16(const uint16_t* __restr
   }
   auto issue = [&](int slot, int step) {
     uint8_t* b = ring + slot * SLOT;
-    lds_dma16(rw, b, wlane + step * KSTEP * BPE2 / 2);
 #pragma unroll
-    for (int q = 0; q < XQ; q++) lds_dma16(rx, b + 1024 + q * 1024, xoff[q] + step * KSTEP * 2);
+    for (int t = 0; t < CT; t++) lds_dma16(rw, b + t * 1024, wlane + 16 * t * rowbytes + step * KSTEP * BPE2 / 2);
+#pragma unroll
+    for (int q = 0; q < XQ; q++) lds_dma16(rx, b + CT * 1024 + q * 1024, xoff[q] + step * KSTEP * 2);
   };
 #pragma unroll
   for (int c = 0; c < R; c++) issue(c, c);
 
-  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t acc[CT];
+#pragma unroll
+  for (int t = 0; t < CT; t++) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < SPW; c++) {
     if (c + 1 < SPW) wait_vm<VMS>();
     else wait_vm<0>();
     const uint8_t* b = ring + (c % R) * SLOT;
-    const u32x4_t wv = ld16(b + lane * 16);
+    u32x4_t wv[CT];
+#pragma unroll
+    for (int t = 0; t < CT; t++) wv[t] = ld16(b + t * 1024 + lane * 16);
     bf16x8_t xa[MF];
 #pragma unroll
     for (int j = 0; j < MF; j++) {
       const int ch = (EPL / 8) * g + j;
-      xa[j] = as_bf16x8(ld16(b + 1024 + nl * XRB + 16 * (ch ^ (nl & (CPR - 1)))));
+      xa[j] = as_bf16x8(ld16(b + CT * 1024 + nl * XRB + 16 * (ch ^ (nl & (CPR - 1)))));
     }
-    const scale_t<WDT> scv = scale_from_raw<WDT>(WDT == W_FP8 ? 0u : svr[c]);
-    bf16x8_t bq[4];
-    dequant16<WDT>(wv, scv, bq);
+    bf16x8_t bq[CT][4];
+#pragma unroll
+    for (int t = 0; t < CT; t++) dequant16<WDT>(wv[t], scale_from_raw<WDT>(WDT == W_FP8 ? 0u : svr[c][t]), bq[t]);
     if (c + R < SPW) {
       // the slot's reads have returned before the refill may overwrite it
       __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       issue(c % R, c + R);
     }
 #pragma unroll
-    for (int j = 0; j < MF; j++) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[j], bq[j], acc, 0, 0, 0);
+    for (int t = 0; t < CT; t++)
+#pragma unroll
+      for (int j = 0; j < MF; j++) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[j], bq[t][j], acc[t], 0, 0, 0);
   }
 
+  // acc[t][i] holds C[m = 4g + i][n = nl] of column tile t
   float* red = reinterpret_cast<float*>(smem);
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 4; i++) red[(wave * 16 + 4 * g + i) * 16 + nl] = acc[i];
+  for (int t = 0; t < CT; t++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) red[((wave * CT + t) * 16 + 4 * g + i) * 16 + nl] = acc[t][i];
   __syncthreads();
-  if (threadIdx.x < 256) {
-    const int m = threadIdx.x >> 4, n = threadIdx.x & 15;
-    const int64_t col = n0 + n;
+  for (int idx = threadIdx.x; idx < CT * 256; idx += 64 * NW) {
+    const int t = idx >> 8, m = (idx >> 4) & 15, n = idx & 15;
+    const int64_t col = n0 + 16 * t + n;
     if (m < M && col < N) {
       float s = 0.0f;
 #pragma unroll
-      for (int wv = 0; wv < NW; wv++) s += red[(wv * 16 + m) * 16 + n];
+      for (int wv = 0; wv < NW; wv++) s += red[((wv * CT + t) * 16 + m) * 16 + n];
       s *= WDT == W_FP8 ? chscale[col] * alpha : alpha;
       y[(int64_t)m * N + col] = (uint16_t)f32_to_bf16_bits(s);
     }
@@ -811,6 +823,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_ring16(const uint16_t* __restr
 // bunches the dequantization work at the end) and 8-wave splits.
 constexpr int RING_NW = 4;
 constexpr int RING_DEPTH = 2;
+// 4 < M <= 16: two 16-column tiles per workgroup share every x chunk, which
+// halves the x traffic from L2 (each workgroup reads the whole x slice).
+constexpr int RING16_CT = 2;
 template <int WDT, int SPW>
 wq_status ring16_go(int64_t M, const uint16_t* x, int64_t N, int64_t K, const uint8_t* w, const void* sc, int gshift,
                     const float* ch, float alpha, uint16_t* y, hipStream_t s) {
@@ -818,12 +833,13 @@ wq_status ring16_go(int64_t M, const uint16_t* x, int64_t N, int64_t K, const ui
   if constexpr (R < 2) {
     return WQ_EUNSUPPORTED;
   } else {
+    constexpr int CT = RING16_CT;
     constexpr int XSLOT = 16 * 4 * (WTraits<WDT>::bits == 4 ? 32 : 16) * 2;
-    const size_t lds = (size_t)RING_NW * R * (1024 + XSLOT);
-    const unsigned grid = (unsigned)((N + 15) / 16);
-    if (allow_lds<k_gemv_ring16<WDT, SPW, R, RING_NW>>(lds) != hipSuccess) return WQ_EHIP;
-    k_gemv_ring16<WDT, SPW, R, RING_NW><<<grid, 64 * RING_NW, lds, s>>>(x, (int)M, N, K, w, sc, gshift, ch, alpha,
-                                                                         y);
+    const size_t lds = (size_t)RING_NW * R * (CT * 1024 + XSLOT);
+    const unsigned grid = (unsigned)((N + 16 * CT - 1) / (16 * CT));
+    if (allow_lds<k_gemv_ring16<WDT, SPW, R, RING_NW, CT>>(lds) != hipSuccess) return WQ_EHIP;
+    k_gemv_ring16<WDT, SPW, R, RING_NW, CT><<<grid, 64 * RING_NW, lds, s>>>(x, (int)M, N, K, w, sc, gshift, ch, alpha,
+                                                                             y);
     return WQ_OK;
   }
 }
