@@ -66,6 +66,24 @@ def test_gemv_ragged(W, kind, M, N, K):
     _check(y, xbits, wdeq, chan)
 
 
+@pytest.mark.parametrize("kind", ["int4", "mxfp4", "e4m3"])
+@pytest.mark.parametrize("M", [1, 4])
+@pytest.mark.parametrize("N,K", [(3205, 1024), (4795, 4096), (4105, 1024), (4097, 2048)])
+def test_gemv_tile_rounds(W, kind, M, N, K):
+    # With 256 CUs: 201 tiles of 16 columns (no half tiles, ragged last tile);
+    # 300 tiles, whose last 44 become 88 tiles of 8 columns (the last one holds
+    # 3 columns); 257 tiles, the last split in two (1 column in the second
+    # half); 257 tiles with 1 column in the last (the second half tile is empty).
+    g = np.random.default_rng(M * 7 + N + K)
+    Wf = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
+    Wf[-3:] *= 30
+    xbits = to_bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    args, wdeq, chan = _prep(W, kind, Wf)
+    banner("gemv tile rounds", kind, M, N, K)
+    y = W.wq_gemm(dev_bf16(xbits), *args, N)
+    _check(y, xbits, wdeq, chan)
+
+
 @pytest.mark.parametrize("group", [32, 64])
 def test_gemv_int4_small_groups(W, group):
     g = np.random.default_rng(group)

@@ -222,9 +222,12 @@ __device__ __forceinline__ u32x4_t bld16(__amdgpu_buffer_rsrc_t r, uint32_t off)
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, (int)voff, 0,
-                                           0, 0);
+// soff: a wave-uniform byte offset added to voff (an SGPR operand, which
+// keeps per-step constants out of the vector ALU)
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, uint32_t voff,
+                                          uint32_t soff = 0) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, (int)voff,
+                                           (int)soff, 0, 0);
 }
 // s_waitcnt with vmcnt <= n, other counters unconstrained (gfx9 encoding).
 template <int N>

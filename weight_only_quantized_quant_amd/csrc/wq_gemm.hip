@@ -492,8 +492,9 @@ __global__ __launch_bounds__(512) void k_gemm8(const uint16_t* __restrict__ x, i
 // ---------------------------------------------------------------------------
 // Decode GEMV, LDS-ring form (M <= 4)
 // ---------------------------------------------------------------------------
-// A workgroup of 4 waves owns 16 output columns; wave w owns the K-slice of
-// SPW steps [w*SPW, (w+1)*SPW).  Packed weights never occupy VGPRs while in
+// A workgroup of 4 waves owns 16 output columns (or 8 over both halves of K,
+// see gemv_ring_tile); wave w owns the K-slice of SPW steps
+// [w*SPW, (w+1)*SPW).  Packed weights never occupy VGPRs while in
 // flight: each step's 16 rows x 64 bytes (1 KB) are fetched by direct-to-LDS
 // buffer loads R steps ahead into a ring of R + 1 slots of the wave, so many
 // steps of every wave are outstanding at once; the extra slot lets each step
@@ -519,90 +520,127 @@ hipError_t allow_lds(size_t bytes) {
   return f;
 }
 
+// Compute units of the current device, queried once per device.
+hipError_t cu_count(int* n) {
+  static int cached[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64 && cached[dev] > 0) {
+    *n = cached[dev];
+    return hipSuccess;
+  }
+  e = hipDeviceGetAttribute(n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (*n <= 0) *n = 1;
+  if (dev >= 0 && dev < 64) cached[dev] = *n;
+  return hipSuccess;
+}
+
 // Ring slots of the LDS ring: one more than the prefetch depth R, so that a
 // refill never targets the slot the current step reads.
 __host__ __device__ constexpr int ring_slots(int spw, int r) { return r < spw ? r + 1 : r; }
 
-template <int WDT, int SPW, int R, int NW, bool SDMA>
-__global__ __launch_bounds__(64 * NW) void k_gemv_ring(const uint16_t* __restrict__ x, int M, int64_t N, int64_t K,
-                                                  const uint8_t* __restrict__ w, const void* __restrict__ sc,
-                                                  int group_shift, const float* __restrict__ chscale,
-                                                  float alpha, uint16_t* __restrict__ y) {
+// One wave's part of a ring tile.  HALF = false: the tile is 16 columns of W
+// over all of K, wave w owns steps [w*SPWE, (w+1)*SPWE) of K.  HALF = true: the
+// tile is 8 columns, and the MFMA's 16 columns are those 8 columns over the two
+// halves of K (MFMA column v: W column v % 8, K half v / 8); the MFMA's rows
+// 0..7 carry the tokens over the first half of K and rows 8..15 over the
+// second, so C[m][v] (v < 8) and C[8 + m][8 + v] are the two halves' partial
+// sums and the other two quadrants are discarded.  Wave w owns steps
+// [w*SPWE, (w+1)*SPWE) of each K half.  Needs M <= 8.
+template <int WDT, int SPWE, int R, int NW, int GSH, bool HALF>
+__device__ __forceinline__ void gemv_ring_tile(const uint16_t* __restrict__ x, int M, int64_t N, int64_t K,
+                                               const uint8_t* __restrict__ w, const void* __restrict__ sc,
+                                               const float* __restrict__ chscale, float alpha,
+                                               uint16_t* __restrict__ y, int64_t n0, uint8_t* smem) {
   constexpr int EPL = WTraits<WDT>::bits == 4 ? 32 : 16;
   constexpr int KSTEP = 4 * EPL;
-  constexpr int KSL = SPW * KSTEP;                            // K of one wave's slice
+  constexpr int KSL = SPWE * KSTEP;                           // K of one wave's slice (per half)
   constexpr int MF = EPL / 8;
   constexpr int BPE2 = WTraits<WDT>::bits == 4 ? 1 : 2;
   constexpr int XROW = KSL * 2;                               // bytes of one x row of the slice
-  static_assert(R <= SPW, "ring larger than the slice");
-  constexpr int NS = ring_slots(SPW, R);
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  constexpr int NR = HALF ? 8 : 16;                           // W rows of the tile
+  static_assert(R <= SPWE, "ring larger than the slice");
+  constexpr int NS = ring_slots(SPWE, R);
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nl = lane & 15, g = lane >> 4;
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  // MFMA column nl: W row wr of the tile, K half hp (the same split for the
+  // MFMA row nl of the x operand)
+  const int wr = HALF ? (nl & 7) : nl, hp = HALF ? nl >> 3 : 0;
   const uint32_t rowbytes = (uint32_t)(K * BPE2 / 2);
-  const int64_t nrows = N - n0 < 16 ? N - n0 : 16;
-  const int gs = gshift_of<WDT>(group_shift);
+  const int64_t nrows = N - n0 < NR ? N - n0 : NR;
+  constexpr int gs = gshift_of<WDT>(GSH);
   const uint32_t spr = (uint32_t)(K >> gs);                  // scales per row
   constexpr int SB = scale_bytes<WDT>();
-  const uint32_t sbrow = (uint32_t)(KSL >> gs) * SB;         // scale bytes per row of the slice
+  constexpr uint32_t sbrow = (uint32_t)(KSL >> gs) * SB;     // scale bytes per row of the slice
   const auto rw = make_rsrc(w + n0 * rowbytes, nrows * rowbytes);
   const auto rs = make_rsrc(reinterpret_cast<const uint8_t*>(sc) + (WDT == W_FP8 ? 0 : n0 * spr * SB),
                             WDT == W_FP8 ? 0 : nrows * spr * SB);
   const auto rx = make_rsrc(x, (int64_t)M * K * 2);
-  const uint32_t kbase = (uint32_t)(wave * KSL);
-  // per-wave LDS: ring | M x rows | scales of the slice (16 rows, row stride srs)
-  const uint32_t srs = sbrow < 16 ? 16 : sbrow;
-  const int sbytes = WDT == W_FP8 ? 0 : 16 * (int)srs;
-  const int wstride = NS * 1024 + M * XROW + ((sbytes + 15) & ~15);
+  const uint32_t khalf = HALF ? (uint32_t)(K / 2) : 0u;
+  const uint32_t kbase = (uint32_t)(wave * KSL);             // within the K half
+  // per-wave LDS: ring | x rows of the slice (HALF: M rows per K half) |
+  // scales of the slice (16 MFMA columns, row stride srs)
+  constexpr int XR = HALF ? 2 : 1;
+  constexpr uint32_t srs = sbrow < 16 ? 16 : sbrow;
+  constexpr int sbytes = WDT == W_FP8 ? 0 : 16 * (int)srs;
+  const int wstride = NS * 1024 + XR * M * XROW + ((sbytes + 15) & ~15);
   uint8_t* ring = smem + wave * wstride;
   uint8_t* xl = ring + NS * 1024;
-  uint8_t* sl = xl + M * XROW;
+  uint8_t* sl = xl + XR * M * XROW;
 
   // 1) scales of the slice.  When a row of the slice holds >= 16 bytes of
   //    scales (a multiple of 16), they arrive by DMA, 16 bytes per lane; for
   //    thinner slices every lane loads its own per-step scales instead (a 16-byte
   //    window could leave the buffer range at the last row and read as zeros).
-  constexpr bool sdma = SDMA;                                // sbrow >= 16, decided by the host
-  uint32_t svr[SPW];
+  constexpr bool sdma = sbrow >= 16;
+  uint32_t svr[SPWE];
   if constexpr (WDT != W_FP8) {
-    if (sdma) {
-      // 16 rows x cpr chunks; one DMA instruction moves 64 of them (1 KB)
-      const int cpr = (int)srs / 16;
+    if constexpr (sdma) {
+      // 16 MFMA columns x cpr chunks; one DMA instruction moves 64 of them (1 KB)
+      constexpr int cpr = (int)srs / 16;
+#pragma unroll
       for (int q = 0; q < (16 * cpr + 63) / 64; q++) {
         const int L = 64 * q + lane;
+        const int v = L / cpr, vr = HALF ? (v & 7) : v, vh = HALF ? v >> 3 : 0;
         if (L < 16 * cpr)
-          lds_dma16(rs, sl + 1024 * q, (uint32_t)(L / cpr) * spr * SB + (kbase >> gs) * SB + 16 * (L % cpr));
+          lds_dma16(rs, sl + 1024 * q,
+                    (uint32_t)vr * spr * SB + ((vh * khalf + kbase) >> gs) * SB + 16 * (L % cpr));
       }
     } else {
 #pragma unroll
-      for (int c = 0; c < SPW; c++)
-        svr[c] = scale_raw_of<WDT>(rs, (uint32_t)nl * spr + ((kbase + c * KSTEP + EPL * g) >> gs));
+      for (int c = 0; c < SPWE; c++)
+        svr[c] = scale_raw_of<WDT>(rs, (uint32_t)wr * spr + ((hp * khalf + kbase + c * KSTEP + EPL * g) >> gs));
     }
   }
-  // 2) x rows of the slice, 1 KB per DMA instruction
+  // 2) x rows of the slice, 1 KB per DMA instruction (HALF: both K halves)
 #pragma unroll
-  for (int r = 0; r < 4; r++)
-    if (r < M)
+  for (int h = 0; h < XR; h++)
 #pragma unroll
-      for (int q = 0; q < (XROW + 1023) / 1024; q++)
-        if (q * 1024 + lane * 16 < XROW)
-          lds_dma16(rx, xl + r * XROW + q * 1024, (uint32_t)(r * (uint32_t)K + kbase + q * 512 + 8 * lane) * 2);
+    for (int r = 0; r < 4; r++)
+      if (r < M)
+#pragma unroll
+        for (int q = 0; q < (XROW + 1023) / 1024; q++)
+          if (q * 1024 + lane * 16 < XROW)
+            lds_dma16(rx, xl + (h * M + r) * XROW + q * 1024,
+                      (uint32_t)(r * (uint32_t)K + h * khalf + kbase + q * 512 + 8 * lane) * 2);
   // 3) the first R weight steps
-  const uint32_t wlane = (uint32_t)nl * rowbytes + (kbase + EPL * g) * BPE2 / 2;
+  const uint32_t wlane = (uint32_t)wr * rowbytes + (hp * khalf + kbase + EPL * g) * BPE2 / 2;
 #pragma unroll
-  for (int c = 0; c < R; c++) lds_dma16(rw, ring + c * 1024, wlane + c * KSTEP * BPE2 / 2);
+  for (int c = 0; c < R; c++) lds_dma16(rw, ring + c * 1024, wlane, c * KSTEP * BPE2 / 2);
 
   f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int xr = nl < M ? nl : 0;
+  const int tok = HALF ? (nl & 7) : nl;                       // token of this lane's x operand row
+  const uint8_t* xrow = xl + (hp * M + (tok < M ? tok : 0)) * XROW;
 #pragma unroll
-  for (int c = 0; c < SPW; c++) {
-    // weight loads issued after step c's: min(R-1, SPW-1-c) (each step issues its
-    // refill after this wait)
-    if (c + R - 1 < SPW) wait_vm<R - 1>();
+  for (int c = 0; c < SPWE; c++) {
+    // weight loads issued after step c's: min(R-1, SPWE-1-c) (each step issues
+    // its refill after this wait)
+    if (c + R - 1 < SPWE) wait_vm<R - 1>();
     else {
-      switch (SPW - 1 - c) {
+      switch (SPWE - 1 - c) {
         case 0: wait_vm<0>(); break;
         case 1: wait_vm<1>(); break;
         case 2: wait_vm<2>(); break;
@@ -613,12 +651,12 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_ring(const uint16_t* __restric
         default: wait_vm<0>(); break;
       }
     }
-    if (c + R < SPW) {
+    if (c + R < SPWE) {
       // step c + R goes to the slot step c - 1 read: that read returned before
       // step c - 1's conversion, and nothing may be scheduled across the
       // barrier (a DMA write is not ordered after an earlier LDS read)
       __builtin_amdgcn_sched_barrier(0);
-      lds_dma16(rw, ring + ((c + R) % NS) * 1024, wlane + (c + R) * KSTEP * BPE2 / 2);
+      lds_dma16(rw, ring + ((c + R) % NS) * 1024, wlane, (c + R) * KSTEP * BPE2 / 2);
     }
     const u32x4_t wv = *reinterpret_cast<const u32x4_t*>(ring + (c % NS) * 1024 + lane * 16);
     scale_t<WDT> scv{};
@@ -638,7 +676,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_ring(const uint16_t* __restric
     bf16x8_t xa[MF];
 #pragma unroll
     for (int j = 0; j < MF; j++)
-      xa[j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(xl + xr * XROW + (c * KSTEP + EPL * g + 8 * j) * 2));
+      xa[j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(xrow + (c * KSTEP + EPL * g + 8 * j) * 2));
     bf16x8_t b[4];
     dequant16<WDT>(wv, scv, b);
 #pragma unroll
@@ -651,17 +689,43 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_ring(const uint16_t* __restric
 #pragma unroll
   for (int i = 0; i < 4; i++) red[(wave * 16 + 4 * g + i) * 16 + nl] = acc[i];
   __syncthreads();
-  if (threadIdx.x < 256) {
-    const int m = threadIdx.x >> 4, n = threadIdx.x & 15;
+  if (threadIdx.x < 16 * NR) {
+    const int m = threadIdx.x / NR, n = threadIdx.x % NR;
     const int64_t col = n0 + n;
     if (m < M && col < N) {
       float s = 0.0f;
 #pragma unroll
-      for (int wv = 0; wv < NW; wv++) s += red[(wv * 16 + m) * 16 + n];
+      for (int wv = 0; wv < NW; wv++) {
+        s += red[(wv * 16 + m) * 16 + n];
+        if constexpr (HALF) s += red[(wv * 16 + 8 + m) * 16 + 8 + n];
+      }
       s *= WDT == W_FP8 ? chscale[col] * alpha : alpha;
       y[(int64_t)m * N + col] = (uint16_t)f32_to_bf16_bits(s);
     }
   }
+}
+
+// GSH: log2 of the INT4 scale group (a template parameter, so that every
+// scale address is a compile-time offset).  Workgroups below nfull take
+// 16-column tiles, the rest 8-column tiles from column 16 * nfull on: the
+// host turns a last, partial round of tiles over the CUs into twice as many
+// half tiles, so that every CU gets the same work.
+template <int WDT, int SPW, int R, int NW, int GSH>
+__global__ __launch_bounds__(64 * NW) void k_gemv_ring(const uint16_t* __restrict__ x, int M, int64_t N, int64_t K,
+                                                  const uint8_t* __restrict__ w, const void* __restrict__ sc,
+                                                  const float* __restrict__ chscale, float alpha,
+                                                  uint16_t* __restrict__ y, int nfull) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int b = (int)blockIdx.x;
+  if constexpr (SPW >= 2) {
+    constexpr int SPH = SPW / 2, RH = R < SPH ? R : SPH;
+    if (b >= nfull) {
+      gemv_ring_tile<WDT, SPH, RH, NW, GSH, true>(x, M, N, K, w, sc, chscale, alpha, y,
+                                                  (int64_t)nfull * 16 + (int64_t)(b - nfull) * 8, smem);
+      return;
+    }
+  }
+  gemv_ring_tile<WDT, SPW, R, NW, GSH, false>(x, M, N, K, w, sc, chscale, alpha, y, (int64_t)b * 16, smem);
 }
 
 // Split of the K loop: T = K / KSTEP steps = S waves x niter iterations x NSTEP.
@@ -704,12 +768,11 @@ void gemv_nstep(const GemvSplit& sp, const uint16_t* x, int64_t M, int64_t N, in
 // L2 by every workgroup).  A row's 16-byte chunks are XOR-swizzled by the row
 // so that the 16 lanes reading one chunk of 16 rows use distinct banks; rows
 // >= M read as zeros.  Scales come from per-lane loads issued up front.
-template <int WDT, int SPW, int R, int NW, int CT>
+template <int WDT, int SPW, int R, int NW, int CT, int GSH>
 __global__ __launch_bounds__(64 * NW) void k_gemv_ring16(const uint16_t* __restrict__ x, int M, int64_t N,
                                                     int64_t K, const uint8_t* __restrict__ w,
-                                                    const void* __restrict__ sc, int group_shift,
-                                                    const float* __restrict__ chscale, float alpha,
-                                                    uint16_t* __restrict__ y) {
+                                                    const void* __restrict__ sc, const float* __restrict__ chscale,
+                                                    float alpha, uint16_t* __restrict__ y) {
   constexpr int EPL = WTraits<WDT>::bits == 4 ? 32 : 16;
   constexpr int KSTEP = 4 * EPL;
   constexpr int KSL = SPW * KSTEP;
@@ -730,7 +793,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_ring16(const uint16_t* __restr
   const int64_t n0 = (int64_t)blockIdx.x * 16 * CT;
   const uint32_t rowbytes = (uint32_t)(K * BPE2 / 2);
   const int64_t nrows = N - n0 < 16 * CT ? N - n0 : 16 * CT;
-  const int gs = gshift_of<WDT>(group_shift);
+  constexpr int gs = gshift_of<WDT>(GSH);
   const uint32_t spr = (uint32_t)(K >> gs);
   constexpr int SB = scale_bytes<WDT>();
   const auto rw = make_rsrc(w + n0 * rowbytes, nrows * rowbytes);
@@ -826,8 +889,8 @@ constexpr int RING_DEPTH = 2;
 // 4 < M <= 16: two 16-column tiles per workgroup share every x chunk, which
 // halves the x traffic from L2 (each workgroup reads the whole x slice).
 constexpr int RING16_CT = 2;
-template <int WDT, int SPW>
-wq_status ring16_go(int64_t M, const uint16_t* x, int64_t N, int64_t K, const uint8_t* w, const void* sc, int gshift,
+template <int WDT, int SPW, int GSH>
+wq_status ring16_go(int64_t M, const uint16_t* x, int64_t N, int64_t K, const uint8_t* w, const void* sc,
                     const float* ch, float alpha, uint16_t* y, hipStream_t s) {
   constexpr int R = SPW < 2 ? SPW : 2;
   if constexpr (R < 2) {
@@ -837,19 +900,31 @@ wq_status ring16_go(int64_t M, const uint16_t* x, int64_t N, int64_t K, const ui
     constexpr int XSLOT = 16 * 4 * (WTraits<WDT>::bits == 4 ? 32 : 16) * 2;
     const size_t lds = (size_t)RING_NW * R * (CT * 1024 + XSLOT);
     const unsigned grid = (unsigned)((N + 16 * CT - 1) / (16 * CT));
-    if (allow_lds<k_gemv_ring16<WDT, SPW, R, RING_NW, CT>>(lds) != hipSuccess) return WQ_EHIP;
-    k_gemv_ring16<WDT, SPW, R, RING_NW, CT><<<grid, 64 * RING_NW, lds, s>>>(x, (int)M, N, K, w, sc, gshift, ch, alpha,
-                                                                             y);
+    if (allow_lds<k_gemv_ring16<WDT, SPW, R, RING_NW, CT, GSH>>(lds) != hipSuccess) return WQ_EHIP;
+    k_gemv_ring16<WDT, SPW, R, RING_NW, CT, GSH><<<grid, 64 * RING_NW, lds, s>>>(x, (int)M, N, K, w, sc, ch, alpha, y);
     return WQ_OK;
   }
 }
 
-template <int WDT, int SPW, int R, bool SDMA>
-wq_status ring_launch(int64_t M, const uint16_t* x, int64_t N, int64_t K, const uint8_t* w, const void* sc, int gshift,
-                      const float* ch, float alpha, uint16_t* y, size_t lds, hipStream_t s) {
-  if (allow_lds<k_gemv_ring<WDT, SPW, R, RING_NW, SDMA>>(lds) != hipSuccess) return WQ_EHIP;
-  const unsigned grid = (unsigned)((N + 15) / 16);
-  k_gemv_ring<WDT, SPW, R, RING_NW, SDMA><<<grid, 64 * RING_NW, lds, s>>>(x, (int)M, N, K, w, sc, gshift, ch, alpha, y);
+template <int WDT, int SPW, int R, int GSH>
+wq_status ring_launch(int64_t M, const uint16_t* x, int64_t N, int64_t K, const uint8_t* w, const void* sc,
+                      const float* ch, float alpha, uint16_t* y, hipStream_t s) {
+  constexpr int KSL = SPW * (WTraits<WDT>::bits == 4 ? 128 : 64);
+  constexpr int sbrow = (KSL >> gshift_of<WDT>(GSH)) * scale_bytes<WDT>();
+  constexpr int sbytes = WDT == W_FP8 ? 0 : 16 * (sbrow < 16 ? 16 : sbrow);
+  const size_t lds = (size_t)RING_NW * (ring_slots(SPW, R) * 1024 + M * KSL * 2 + ((sbytes + 15) & ~15));
+  if (allow_lds<k_gemv_ring<WDT, SPW, R, RING_NW, GSH>>(lds) != hipSuccess) return WQ_EHIP;
+  // all tiles are resident at once and dispatched round by round over the
+  // CUs; a last round that covers at most half of the CUs becomes twice as
+  // many 8-column tiles, one per CU
+  const int64_t tiles = (N + 15) / 16;
+  int ncu = 0;
+  if (cu_count(&ncu) != hipSuccess) return WQ_EHIP;
+  const int64_t last = tiles % ncu;
+  const int64_t nfull = SPW >= 2 && last > 0 && 2 * last <= ncu ? tiles - last : tiles;
+  const unsigned grid = (unsigned)(nfull + 2 * (tiles - nfull));
+  k_gemv_ring<WDT, SPW, R, RING_NW, GSH><<<grid, 64 * RING_NW, lds, s>>>(x, (int)M, N, K, w, sc, ch, alpha, y,
+                                                                       (int)nfull);
   return WQ_OK;
 }
 
@@ -857,59 +932,57 @@ wq_status ring_launch(int64_t M, const uint16_t* x, int64_t N, int64_t K, const 
 // steps take longer and a deeper ring keeps more bytes in flight (measured at
 // M = 4: one more step for 4-bit weights, two more for 8-bit; at M = 2 the
 // shallow ring is still faster).
-template <int WDT, int SPW>
-wq_status ring_go(int64_t M, const uint16_t* x, int64_t N, int64_t K, const uint8_t* w, const void* sc, int gshift,
+template <int WDT, int SPW, int GSH>
+wq_status ring_go(int64_t M, const uint16_t* x, int64_t N, int64_t K, const uint8_t* w, const void* sc,
                   const float* ch, float alpha, uint16_t* y, hipStream_t s) {
   constexpr int R1 = SPW < RING_DEPTH ? SPW : RING_DEPTH;
   constexpr int RM0 = RING_DEPTH + (WTraits<WDT>::bits == 8 ? 2 : 1);
   constexpr int RM = SPW < RM0 ? SPW : RM0;
-  constexpr int KSL = SPW * (WTraits<WDT>::bits == 4 ? 128 : 64);
-  const int gs = gshift_of<WDT>(gshift);
-  const int sbrow = (KSL >> gs) * scale_bytes<WDT>();
-  const int sbytes = WDT == W_FP8 ? 0 : 16 * (sbrow < 16 ? 16 : sbrow);
-  const bool shallow = M <= 2;
-  const int r = shallow ? R1 : RM;
-  const size_t lds = (size_t)RING_NW * (ring_slots(SPW, r) * 1024 + M * KSL * 2 + ((sbytes + 15) & ~15));
-  if (shallow) {
-    return sbrow >= 16 ? ring_launch<WDT, SPW, R1, true>(M, x, N, K, w, sc, gshift, ch, alpha, y, lds, s)
-                       : ring_launch<WDT, SPW, R1, false>(M, x, N, K, w, sc, gshift, ch, alpha, y, lds, s);
+  if (M <= 2) return ring_launch<WDT, SPW, R1, GSH>(M, x, N, K, w, sc, ch, alpha, y, s);
+  return ring_launch<WDT, SPW, RM, GSH>(M, x, N, K, w, sc, ch, alpha, y, s);
+}
+
+// The ring forms, when K splits into 4 wave slices of 1, 2, 4, 8 or 16 steps;
+// false when the shape needs the general GEMV.
+template <int WDT, int GSH>
+bool ring_path(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w, const void* sc,
+               const float* ch, float alpha, uint16_t* y, hipStream_t s, wq_status& st) {
+  constexpr int KSTEP = WTraits<WDT>::bits == 4 ? 128 : 64;
+  if (K % (KSTEP * RING_NW) || 16 * K * 2 > 0x7FFFFFF0LL) return false;
+  const int64_t spw = K / (KSTEP * RING_NW);
+  if (M <= 4) {
+    switch (spw) {
+      case 1: st = ring_go<WDT, 1, GSH>(M, x, N, K, w, sc, ch, alpha, y, s); return true;
+      case 2: st = ring_go<WDT, 2, GSH>(M, x, N, K, w, sc, ch, alpha, y, s); return true;
+      case 4: st = ring_go<WDT, 4, GSH>(M, x, N, K, w, sc, ch, alpha, y, s); return true;
+      case 8: st = ring_go<WDT, 8, GSH>(M, x, N, K, w, sc, ch, alpha, y, s); return true;
+      case 16: st = ring_go<WDT, 16, GSH>(M, x, N, K, w, sc, ch, alpha, y, s); return true;
+      default: return false;
+    }
   }
-  return sbrow >= 16 ? ring_launch<WDT, SPW, RM, true>(M, x, N, K, w, sc, gshift, ch, alpha, y, lds, s)
-                     : ring_launch<WDT, SPW, RM, false>(M, x, N, K, w, sc, gshift, ch, alpha, y, lds, s);
+  switch (spw) {
+    case 2: st = ring16_go<WDT, 2, GSH>(M, x, N, K, w, sc, ch, alpha, y, s); return true;
+    case 4: st = ring16_go<WDT, 4, GSH>(M, x, N, K, w, sc, ch, alpha, y, s); return true;
+    case 8: st = ring16_go<WDT, 8, GSH>(M, x, N, K, w, sc, ch, alpha, y, s); return true;
+    case 16: st = ring16_go<WDT, 16, GSH>(M, x, N, K, w, sc, ch, alpha, y, s); return true;
+    default: return false;
+  }
 }
 
 template <int WDT>
 wq_status launch_gemv(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w, const void* sc, int group,
                       const float* ch, float alpha, uint16_t* y, hipStream_t s) {
   constexpr int KSTEP = WTraits<WDT>::bits == 4 ? 128 : 64;
-  const int gshift = group == 32 ? 5 : group == 64 ? 6 : 7;
-  if (M <= 4 && K % (KSTEP * RING_NW) == 0 && 16 * K * 2 <= 0x7FFFFFF0LL) {
-    const int64_t spw = K / (KSTEP * RING_NW);
-    if (spw == 1 || spw == 2 || spw == 4 || spw == 8 || spw == 16) {
-      wq_status st;
-      switch (spw) {
-        case 1: st = ring_go<WDT, 1>(M, x, N, K, w, sc, gshift, ch, alpha, y, s); break;
-        case 2: st = ring_go<WDT, 2>(M, x, N, K, w, sc, gshift, ch, alpha, y, s); break;
-        case 4: st = ring_go<WDT, 4>(M, x, N, K, w, sc, gshift, ch, alpha, y, s); break;
-        case 8: st = ring_go<WDT, 8>(M, x, N, K, w, sc, gshift, ch, alpha, y, s); break;
-        default: st = ring_go<WDT, 16>(M, x, N, K, w, sc, gshift, ch, alpha, y, s); break;
-      }
-      return st != WQ_OK ? st : wq_launch_status();
-    }
+  wq_status st = WQ_OK;
+  bool ring;
+  if constexpr (WDT == W_INT4 || WDT == W_UINT4) {
+    ring = group == 32   ? ring_path<WDT, 5>(x, M, N, K, w, sc, ch, alpha, y, s, st)
+           : group == 64 ? ring_path<WDT, 6>(x, M, N, K, w, sc, ch, alpha, y, s, st)
+                         : ring_path<WDT, 7>(x, M, N, K, w, sc, ch, alpha, y, s, st);
+  } else {
+    ring = ring_path<WDT, 0>(x, M, N, K, w, sc, ch, alpha, y, s, st);
   }
-  if (M > 4 && M <= 16 && K % (KSTEP * RING_NW) == 0 && 16 * K * 2 <= 0x7FFFFFF0LL) {
-    const int64_t spw = K / (KSTEP * RING_NW);
-    if (spw == 2 || spw == 4 || spw == 8 || spw == 16) {
-      wq_status st;
-      switch (spw) {
-        case 2: st = ring16_go<WDT, 2>(M, x, N, K, w, sc, gshift, ch, alpha, y, s); break;
-        case 4: st = ring16_go<WDT, 4>(M, x, N, K, w, sc, gshift, ch, alpha, y, s); break;
-        case 8: st = ring16_go<WDT, 8>(M, x, N, K, w, sc, gshift, ch, alpha, y, s); break;
-        default: st = ring16_go<WDT, 16>(M, x, N, K, w, sc, gshift, ch, alpha, y, s); break;
-      }
-      return st != WQ_OK ? st : wq_launch_status();
-    }
-  }
+  if (ring) return st != WQ_OK ? st : wq_launch_status();
   constexpr int MAXSTEP = WTraits<WDT>::bits == 4 ? 4 : 8;
   // the per-workgroup buffer resources address 16*TN rows (< 2^31 bytes)
   if (32 * K * (WTraits<WDT>::bits / 4) / 2 > 0x7FFFFFF0LL || M * K * 2 > 0x7FFFFFF0LL) return WQ_EINVAL;
