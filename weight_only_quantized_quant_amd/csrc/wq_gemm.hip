@@ -254,14 +254,16 @@ __global__ __launch_bounds__(512) void k_gemv(const uint16_t* __restrict__ x, in
 // Prefill GEMM, 8-wave form
 // ---------------------------------------------------------------------------
 // 256x256 output tile per workgroup of 8 waves (2 along M x 4 along N, each
-// 128x64 with MFMA 32x32x16 bf16), K step 64, three LDS stages.  Two waves share
+// 128x64 with MFMA 32x32x16 bf16), K step 64, three LDS stages (four were
+// measured no faster for 4-bit weights).  Two waves share
 // each SIMD, so one wave's MFMAs overlap the other's dequantization and LDS
-// reads.  Tiles arrive by direct-to-LDS buffer loads issued two K steps ahead;
-// one barrier per step both publishes the step's tiles and retires the reads
-// of the stage the next loads overwrite.  x rows are 128 bytes in LDS with
-// their 16-byte chunks XOR-swizzled by row (chunk c of row r sits at c ^ (r & 7)),
-// which keeps the 32 lanes reading 32 rows of one chunk on distinct banks; W
-// rows are swizzled the same way at their 16-byte chunk granularity.
+// reads.  Tiles arrive by direct-to-LDS buffer loads issued NSTAGE - 1 K steps
+// ahead; one barrier per step both publishes a step's tiles and retires the
+// reads of the stage the next loads overwrite.  x rows are 128 bytes in LDS with
+// their 16-byte chunks XOR-swizzled by row (chunk c of row r sits at
+// c ^ ((r >> 1) & 7)); W rows are swizzled at their 16-byte chunk granularity.
+// Both placements were measured on gfx950 to read their fragments (32 rows x 2
+// chunks) without LDS bank conflicts; c ^ (r & 7) takes about 1.7 times as long.
 // Rows past M or N read as zeros through the buffer range; their results are
 // not stored.
 template <int WDT>
@@ -275,13 +277,15 @@ struct Gemm8 {
   static constexpr int LDS = NSTAGE * STAGE;
   static constexpr int B_DMA = B_TILE / 1024 / 8;               // 1 KB DMA instructions per wave
   static constexpr int LPR = wbytes / 16;                       // 16-byte chunks per W row
-  // vector-memory instructions one step issues per lane: tile DMAs, then scales
-  static constexpr int VM_STEP = 4 + B_DMA + (WTraits<WDT>::bits == 4 ? 2 : 0);
+  // vector-memory instructions one step issues per lane: tile DMAs, scale loads
+  static constexpr int VM_T = 4 + B_DMA;
+  static constexpr int VM_S = WTraits<WDT>::bits == 4 ? 2 : 0;
 };
-// W rows of 32 or 64 bytes: chunk c of row r sits at c ^ bswz(r), which spreads
-// 8 consecutive rows read at one chunk over distinct banks.
+// x rows (128 bytes): chunk c of row r sits at c ^ aswz(r).
+__device__ __forceinline__ int aswz(int r) { return (r >> 1) & 7; }
+// W rows of 32 or 64 bytes: chunk c of row r sits at c ^ bswz(r).
 template <int LPR>
-__device__ __forceinline__ int bswz(int r) { return LPR == 2 ? (r >> 2) & 1 : (r >> 1) & 3; }
+__device__ __forceinline__ int bswz(int r) { return LPR == 2 ? (r >> 3) & 1 : (r >> 1) & 3; }
 
 template <int WDT>
 __global__ __launch_bounds__(512) void k_gemm8(const uint16_t* __restrict__ x, int64_t M, int64_t N, int64_t K,
@@ -312,7 +316,7 @@ __global__ __launch_bounds__(512) void k_gemm8(const uint16_t* __restrict__ x, i
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     const int r = 8 * (wave * 4 + i) + (lane >> 3);
-    const int c = (lane & 7) ^ (r & 7);
+    const int c = (lane & 7) ^ aswz(r);
     a_off[i] = (uint32_t)r * (uint32_t)(K * 2) + 16 * c;
   }
   // B: rows of wbytes, lanes in row order, chunks swizzled by row.
@@ -369,38 +373,55 @@ __global__ __launch_bounds__(512) void k_gemm8(const uint16_t* __restrict__ x, i
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
 
-  // Software pipeline.  Step k's loads (group k) go to stage k % 3, two steps
-  // ahead; at the top of step k groups <= k + 1 are resident and visible.  The
-  // MFMAs of step k run on W fragments converted during step k - 1, and each of
-  // its four k16 slices converts the matching quarter of step k + 1's fragments,
-  // so dequantization overlaps the matrix work inside the wave.  The barrier at
-  // the end of step k publishes group k + 2 and retires every read of stage
-  // k % 3, which step k + 1 refills with group k + 3.  The loop is unrolled by
-  // two with ping-pong registers (no register copies; on the last step the
-  // extra conversion reads a stale stage and is unused).
-  static_assert(C::NSTAGE == 3, "two steps of prefetch");
+  // Software pipeline.  Group k (step k's tiles) goes to stage k % NSTAGE,
+  // issued at the top of step k - NSTAGE + 1; the scales of group k are loaded
+  // at the top of step k - 2.  The MFMAs of step k run on A from LDS and on W
+  // fragments converted during step k - 1, and each of its four k16 slices
+  // converts the matching quarter of step k + 1's fragments, so dequantization
+  // overlaps the matrix work inside the wave.  The wait and barrier at the end
+  // of step k publish group k + 2 (needed by step k + 1's conversion) and
+  // retire every read of stage k % NSTAGE, which step k + 1 refills.  The loop
+  // is unrolled by two with ping-pong registers (no register copies; on the
+  // last step the extra conversion reads a stale stage and is unused).
+  constexpr int NST = C::NSTAGE;
+  static_assert(NST == 3 || NST == 4, "two or three steps of prefetch");
   const int nk = (int)(K / C::BK);
   uint32_t sa[2], sb[2] = {0u, 0u};
+  // issue order: t0 s0 t1 [t2] s1, so that step 0's closing wait sees the
+  // same queue as every later step's
   issue(0, 0);
 #pragma unroll
   for (int j = 0; j < 2; j++) sa[j] = scale_raw(j, 0);
+  if (nk > 1) issue(1, C::BK);
+  if (NST == 4 && nk > 2) issue(2, 2 * C::BK);
   if (nk > 1) {
-    issue(1, C::BK);
 #pragma unroll
     for (int j = 0; j < 2; j++) sb[j] = scale_raw(j, C::BK);
   }
   wait_vm<0>();
   tile_barrier();
 
+  // 4-bit W: the lane's 16-byte chunk of each column subtile, read once per
+  // step (one 16-byte LDS read instead of four 4-byte ones)
+  auto wchunk = [&](const uint8_t* B, u32x4_t (&wc)[2]) {
+    if constexpr (WTraits<WDT>::bits == 4) {
+#pragma unroll
+      for (int j = 0; j < 2; j++) {
+        const int br = wn * 64 + 32 * j + l32;
+        wc[j] = ld16(B + br * C::wbytes + 16 * (h ^ bswz<LPR>(br)));
+      }
+    }
+  };
   // quarter q (k16 slice q) of a step's W fragments for both column subtiles
-  auto dequant_q = [&](const uint8_t* B, int q, const scale_t<WDT> (&cs)[2], bf16x8_t (&out)[4][2]) {
+  auto dequant_q = [&](const uint8_t* B, const u32x4_t (&wc)[2], int q, const scale_t<WDT> (&cs)[2],
+                       bf16x8_t (&out)[4][2]) {
 #pragma unroll
     for (int j = 0; j < 2; j++) {
       const int br = wn * 64 + 32 * j + l32;
       const uint8_t* bp = B + br * C::wbytes;
       const int sw = bswz<LPR>(br);
       if constexpr (WTraits<WDT>::bits == 4) {
-        const uint32_t wd = *reinterpret_cast<const uint32_t*>(bp + 16 * (h ^ sw) + 4 * q);
+        const uint32_t wd = wc[j][q];
         uint32_t o[4];
         if constexpr (WDT == W_INT4) dq_int4_word(wd, cs[j], o);
         else if constexpr (WDT == W_NV4) dq_nv4_word(wd, q < 2 ? cs[j].lo : cs[j].hi, o);
@@ -419,41 +440,52 @@ __global__ __launch_bounds__(512) void k_gemm8(const uint16_t* __restrict__ x, i
     scale_t<WDT> c0[2];
 #pragma unroll
     for (int j = 0; j < 2; j++) c0[j] = scale_val(sa[j]);
+    u32x4_t wc[2];
+    wchunk(lds + C::A_TILE, wc);
 #pragma unroll
-    for (int q = 0; q < 4; q++) dequant_q(lds + C::A_TILE, q, c0, ba);
+    for (int q = 0; q < 4; q++) dequant_q(lds + C::A_TILE, wc, q, c0, ba);
   }
 
   int stage = 0;
   auto step = [&](int kt, bf16x8_t (&bcur)[4][2], bf16x8_t (&bnext)[4][2], uint32_t (&snext)[2],
                   uint32_t (&sload)[2]) {
-    const int st1 = stage == 2 ? 0 : stage + 1;
-    const int st2 = st1 == 2 ? 0 : st1 + 1;
+    const int st1 = stage == NST - 1 ? 0 : stage + 1;
+    const int stl = stage == 0 ? NST - 1 : stage - 1;        // stage of group kt + NST - 1
     scale_t<WDT> cn[2];
 #pragma unroll
     for (int j = 0; j < 2; j++) cn[j] = scale_val(snext[j]);
+    if (kt + NST - 1 < nk) issue(stl, (int64_t)(kt + NST - 1) * C::BK);
     if (kt + 2 < nk) {
-      issue(st2, (int64_t)(kt + 2) * C::BK);
 #pragma unroll
       for (int j = 0; j < 2; j++) sload[j] = scale_raw(j, (int64_t)(kt + 2) * C::BK);
     }
     const uint8_t* A = lds + stage * C::STAGE;
     const uint8_t* Bn = lds + st1 * C::STAGE + C::A_TILE;
+    u32x4_t wc[2];
+    wchunk(Bn, wc);
 #pragma unroll
     for (int s4 = 0; s4 < 4; s4++) {
       bf16x8_t af[4];
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const int r = wm * 128 + 32 * i + l32;
-        af[i] = as_bf16x8(ld16(A + r * 128 + (((4 * h + s4) ^ (r & 7)) << 4)));
+        af[i] = as_bf16x8(ld16(A + r * 128 + (((4 * h + s4) ^ aswz(r)) << 4)));
       }
-      dequant_q(Bn, s4, cn, bnext);
+      dequant_q(Bn, wc, s4, cn, bnext);
 #pragma unroll
       for (int i = 0; i < 4; i++)
 #pragma unroll
         for (int j = 0; j < 2; j++)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bcur[s4][j], acc[i][j], 0, 0, 0);
     }
-    wait_vm<0>();
+    // group kt + 2 complete: with four stages the loads queued behind it are
+    // the scales of group kt + 1, group kt + 3 and the scales of group kt + 2
+    if constexpr (NST == 4) {
+      if (kt + 3 < nk) wait_vm<C::VM_T + 2 * C::VM_S>();
+      else wait_vm<0>();
+    } else {
+      wait_vm<0>();
+    }
     tile_barrier();
     stage = st1;
   };

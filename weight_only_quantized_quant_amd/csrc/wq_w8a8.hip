@@ -122,8 +122,10 @@ constexpr int GW_TILE = GBN * GBK;                       // 32 KB of E4M3 weight
 constexpr int GX_TILE = GBM * GBK;                       // 32 KB of E4M3 activation rows
 constexpr int GSTAGE = GW_TILE + GX_TILE;
 constexpr int GLDS = 2 * GSTAGE;                         // 128 KB
-// 128-byte rows: chunk c of row r sits at c ^ ((r >> 1) & 7), so the 16 rows
-// that 16 lanes read at one chunk cover all 64 banks
+// 128-byte rows: chunk c of row r sits at c ^ ((r >> 1) & 7).  The counters
+// report LDS bank conflicts for the fragment reads (16 rows x 4 chunk pairs)
+// with this placement and none with c ^ ((r ^ (r >> 3)) & 7), but the GEMM
+// measured about 5 % faster with this one.
 __device__ __forceinline__ int gswz(int r) { return (r >> 1) & 7; }
 
 __device__ __forceinline__ i32x8_t ld_frag(const uint8_t* tile, int r, int q) {
