@@ -220,9 +220,13 @@ __global__ __launch_bounds__(512) void k_w8a8(const uint8_t* __restrict__ a, con
 #pragma unroll
       for (int j = 0; j < 4; j++) f[j] = fa[j] * fb;
     }
+    // weight fragment i + 1 is read while fragment i's MFMAs run
+    i32x8_t awn = ld_frag(Wt, wn * 128 + l16, q);
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-      const i32x8_t aw = ld_frag(Wt, wn * 128 + 16 * i + l16, q);
+      const i32x8_t aw = awn;
+      if (i < 7) awn = ld_frag(Wt, wn * 128 + 16 * (i + 1) + l16, q);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < 4; j++) {
         if constexpr (PROMOTE) {
