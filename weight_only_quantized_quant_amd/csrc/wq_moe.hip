@@ -21,7 +21,7 @@
 // one mask then give four table indices in k order.
 //
 // Grouped GEMM: 256 x 256 tiles of (rows of one expert) x (output channels),
-// 8 waves of 128 x 64, K step 128 = one INT4 group, three LDS stages filled by
+// 8 waves of 256 x 32, K step 128 = one INT4 group, three LDS stages filled by
 // direct-to-LDS loads two steps ahead; the activation rows are gathered through
 // row_token.
 // v_mfma_scale_f32_32x32x64_f8f6f4 with neutral block scales multiplies the
@@ -220,6 +220,11 @@ constexpr int MNSTAGE = 3;                              // loads run two steps a
 constexpr int MLDS = MNSTAGE * MSTAGE;                  // 144 KB
 // W rows of 64 bytes: chunk c of row r sits at c ^ ((r >> 1) & 3)
 __device__ __forceinline__ int mbswz(int r) { return (r >> 1) & 3; }
+// The 8 waves all lie along N, each owning 256 rows x 32 channels (8 MFMA
+// tiles of 32x32): every W fragment is converted through its table once per
+// workgroup (with 2 x 4 waves the two M-halves converted each fragment twice),
+// at twice the activation fragment reads from LDS.
+constexpr int MWN = 8, MTN = MBN / MWN, MMI = MBM / 32;
 
 __global__ __launch_bounds__(512) void k_moe_gemm(const uint8_t* __restrict__ x8, int64_t T,
                                                   const float* __restrict__ a_scale,
@@ -233,7 +238,7 @@ __global__ __launch_bounds__(512) void k_moe_gemm(const uint8_t* __restrict__ x8
   __shared__ float rscale[MBM];                         // a_scale of each row of the tile
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wn = wave;
   const int l32 = lane & 31, h = lane >> 5;
 
   const int nwg = (int)gridDim.x;
@@ -309,47 +314,42 @@ __global__ __launch_bounds__(512) void k_moe_gemm(const uint8_t* __restrict__ x8
     for (int i = 0; i < 2; i++) lds_dma16(rb, B + (wave * 2 + i) * 1024, b_off[i] + (uint32_t)(k0 / 2));
   };
 
-  // group scales of this lane's two columns
-  const uint8_t* s8row[2];
-#pragma unroll
-  for (int j = 0; j < 2; j++) {
-    int64_t n = n0 + wn * 64 + 32 * j + l32;
-    n = n < N ? n : N - 1;
-    s8row[j] = s8 + ((int64_t)e * N + n) * G;
-  }
+  // group scales of this lane's column
+  int64_t ncol = n0 + wn * MTN + l32;
+  ncol = ncol < N ? ncol : N - 1;
+  const uint8_t* s8row = s8 + ((int64_t)e * N + ncol) * G;
 
-  f32x16_t acc[4][2];
+  f32x16_t acc[MMI];
 #pragma unroll
-  for (int i = 0; i < 4; i++)
+  for (int i = 0; i < MMI; i++)
 #pragma unroll
-    for (int j = 0; j < 2; j++)
-#pragma unroll
-      for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
+    for (int r = 0; r < 16; r++) acc[i][r] = 0.0f;
 
-  // B operands of half s2 of a step (K 64): 32 E4M3 codes per lane and column
-  auto lut_half = [&](const uint8_t* B, int s2, const Lut (&L)[2], i32x8_t (&bf)[2]) {
+  // B operand of half s2 of a step (K 64): 32 E4M3 codes of the lane's column
+  auto lut_half = [&](const uint8_t* B, int s2, const Lut& L, i32x8_t& bf) {
+    const int br = wn * MTN + l32;
+    const u32x4_t pw = ld16(B + br * 64 + 16 * ((2 * s2 + h) ^ mbswz(br)));
+    uint32_t d[8];
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-      const int br = wn * 64 + 32 * j + l32;
-      const u32x4_t pw = ld16(B + br * 64 + 16 * ((2 * s2 + h) ^ mbswz(br)));
-      uint32_t d[8];
-#pragma unroll
-      for (int q = 0; q < 4; q++) lut_word(pw[q], L[j], d[2 * q], d[2 * q + 1]);
-      bf[j] = i32x8_t{(int)d[0], (int)d[1], (int)d[2], (int)d[3], (int)d[4], (int)d[5], (int)d[6], (int)d[7]};
-    }
+    for (int q = 0; q < 4; q++) lut_word(pw[q], L, d[2 * q], d[2 * q + 1]);
+    bf = i32x8_t{(int)d[0], (int)d[1], (int)d[2], (int)d[3], (int)d[4], (int)d[5], (int)d[6], (int)d[7]};
   };
-  auto mfma_half = [&](const uint8_t* A, int s2, const i32x8_t (&bf)[2]) {
+  // A operand of row tile i and half s2 of the step in stage A
+  auto load_a = [&](const uint8_t* A, int s2, int i) -> i32x8_t {
+    const int r = 32 * i + l32;
+    const int c0 = 4 * s2 + 2 * h;
+    const u32x4_t p0 = ld16(A + r * 128 + ((c0 ^ (r & 7)) << 4));
+    const u32x4_t p1 = ld16(A + r * 128 + (((c0 + 1) ^ (r & 7)) << 4));
+    return i32x8_t{(int)p0[0], (int)p0[1], (int)p0[2], (int)p0[3], (int)p1[0], (int)p1[1], (int)p1[2], (int)p1[3]};
+  };
+  // the 8 MFMAs of half s2; tile i + 1's operand is read while tile i's MFMA runs
+  auto mfma_half = [&](const uint8_t* A, int s2, const i32x8_t& bf) {
+    i32x8_t an = load_a(A, s2, 0);
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int r = wm * 128 + 32 * i + l32;
-      const int c0 = 4 * s2 + 2 * h;
-      const u32x4_t p0 = ld16(A + r * 128 + ((c0 ^ (r & 7)) << 4));
-      const u32x4_t p1 = ld16(A + r * 128 + (((c0 + 1) ^ (r & 7)) << 4));
-      const i32x8_t af = i32x8_t{(int)p0[0], (int)p0[1], (int)p0[2], (int)p0[3],
-                                 (int)p1[0], (int)p1[1], (int)p1[2], (int)p1[3]};
-#pragma unroll
-      for (int j = 0; j < 2; j++)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf[j], acc[i][j], 0, 0, 0, 127, 0, 127);
+    for (int i = 0; i < MMI; i++) {
+      const i32x8_t af = an;
+      if (i + 1 < MMI) an = load_a(A, s2, i + 1);
+      acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, acc[i], 0, 0, 0, 127, 0, 127);
     }
   };
 
@@ -361,22 +361,17 @@ __global__ __launch_bounds__(512) void k_moe_gemm(const uint8_t* __restrict__ x8
   // barrier at the end of step k publishes group k + 2 and retires every read
   // of stage k % 3, which step k + 1 then refills with group k + 3.
   const int nk = (int)(K / MBK);
-  uint32_t sn[2], sn2[2] = {0u, 0u};                   // raw s8 of steps k + 1, k + 2
+  uint32_t sn = 0u, sn2 = 0u;                           // raw s8 of steps k + 1, k + 2
   issue(0, 0);
-  uint32_t s0[2];
-#pragma unroll
-  for (int j = 0; j < 2; j++) s0[j] = s8row[j][0];
+  const uint32_t s0 = s8row[0];
   if (nk > 1) {
     issue(1, MBK);
-#pragma unroll
-    for (int j = 0; j < 2; j++) sn[j] = s8row[j][1];
+    sn = s8row[1];
   }
   wait_vm<0>();
   __syncthreads();                                      // also publishes rscale
-  Lut Lc[2];
-#pragma unroll
-  for (int j = 0; j < 2; j++) Lc[j] = make_lut(s0[j]);
-  i32x8_t bc[2], bn[2];
+  Lut Lc = make_lut(s0);
+  i32x8_t bc, bn;
   lut_half(lds + MA_TILE, 0, Lc, bc);
 
   int stage = 0;
@@ -385,21 +380,18 @@ __global__ __launch_bounds__(512) void k_moe_gemm(const uint8_t* __restrict__ x8
     const int st2 = st1 == 2 ? 0 : st1 + 1;
     if (kt + 2 < nk) {
       issue(st2, (int64_t)(kt + 2) * MBK);
-#pragma unroll
-      for (int j = 0; j < 2; j++) sn2[j] = s8row[j][kt + 2];
+      sn2 = s8row[kt + 2];
     }
     // (on the last step the second conversion reads a stale stage; unused)
     const uint8_t* A = lds + stage * MSTAGE;
     lut_half(A + MA_TILE, 1, Lc, bn);
     mfma_half(A, 0, bc);
-#pragma unroll
-    for (int j = 0; j < 2; j++) Lc[j] = make_lut(sn[j]);
+    Lc = make_lut(sn);
     lut_half(lds + st1 * MSTAGE + MA_TILE, 0, Lc, bc);
     mfma_half(A, 1, bn);
     wait_vm<0>();
     tile_barrier();
-#pragma unroll
-    for (int j = 0; j < 2; j++) sn[j] = sn2[j];
+    sn = sn2;
     stage = st1;
   }
 
@@ -408,24 +400,16 @@ __global__ __launch_bounds__(512) void k_moe_gemm(const uint8_t* __restrict__ x8
   // past the expert's end are dropped by the hardware and offsets stay 32-bit.
   const auto ry = make_rsrc(y + r0 * N, (r1 - r0) * N * 2);
   const uint32_t rowb = (uint32_t)(N * 2);
-  float cs[2];
-  uint32_t cb[2];
+  const int64_t col = n0 + wn * MTN + l32;
+  const float cs = col < N ? ch[(int64_t)e * N + col] : 0.0f;
+  const uint32_t cb = col < N ? (uint32_t)(col * 2) : 0x80000000u;   // columns past N: out of range
 #pragma unroll
-  for (int j = 0; j < 2; j++) {
-    const int64_t col = n0 + wn * 64 + 32 * j + l32;
-    cs[j] = col < N ? ch[(int64_t)e * N + col] : 0.0f;
-    cb[j] = col < N ? (uint32_t)(col * 2) : 0x80000000u;   // columns past N: out of range
-  }
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
+  for (int i = 0; i < MMI; i++) {
 #pragma unroll
     for (int r = 0; r < 16; r++) {
-      const int lr = wm * 128 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-      const float rs = rscale[lr];
-      const uint32_t pr = pack_bf16x2(acc[i][0][r] * (rs * cs[0]), acc[i][1][r] * (rs * cs[1]));
-      const uint32_t off = (uint32_t)lr * rowb;
-      __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(pr & 0xFFFFu), ry, (int)(off + cb[0]), 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(pr >> 16), ry, (int)(off + cb[1]), 0, 0);
+      const int lr = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+      const uint32_t v = f32_to_bf16_bits(acc[i][r] * (rscale[lr] * cs));
+      __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, ry, (int)((uint32_t)lr * rowb + cb), 0, 0);
     }
   }
 }
