@@ -975,17 +975,17 @@ wq_status ring_launch(int64_t M, const uint16_t* x, int64_t N, int64_t K, const 
   return WQ_OK;
 }
 
-// Loads run RING_DEPTH steps ahead for one or two tokens; with 3-4 tokens the
-// steps take longer and a deeper ring keeps more bytes in flight (measured at
-// M = 4: one more step for 4-bit weights, two more for 8-bit; at M = 2 the
-// shallow ring is still faster).
+// Loads run RING_DEPTH steps ahead for up to three tokens; with four tokens
+// the steps take longer and a deeper ring keeps more bytes in flight (measured
+// at M = 4: one more step for 4-bit weights, two more for 8-bit; at M = 3 the
+// shallow ring is faster, 10.7 against 11.6 us for INT4).
 template <int WDT, int SPW, int GSH>
 wq_status ring_go(int64_t M, const uint16_t* x, int64_t N, int64_t K, const uint8_t* w, const void* sc,
                   const float* ch, float alpha, uint16_t* y, hipStream_t s) {
   constexpr int R1 = SPW < RING_DEPTH ? SPW : RING_DEPTH;
   constexpr int RM0 = RING_DEPTH + (WTraits<WDT>::bits == 8 ? 2 : 1);
   constexpr int RM = SPW < RM0 ? SPW : RM0;
-  if (M <= 2) return ring_launch<WDT, SPW, R1, GSH>(M, x, N, K, w, sc, ch, alpha, y, s);
+  if (M <= 3) return ring_launch<WDT, SPW, R1, GSH>(M, x, N, K, w, sc, ch, alpha, y, s);
   return ring_launch<WDT, SPW, RM, GSH>(M, x, N, K, w, sc, ch, alpha, y, s);
 }
 
