@@ -279,6 +279,7 @@ struct Gemm8 {
   static constexpr int WM = 8 / WN;
   static constexpr int TM = BM / WM, TN = BN / WN;            // rows and columns per wave
   static constexpr int MI = TM / 32, NJ = TN / 32;
+  static constexpr bool PREFETCH_A = WN == 8;
   static constexpr int NSTAGE = 3;                              // loads run NSTAGE - 1 steps ahead
   static constexpr int wbytes = BK * WTraits<WDT>::bits / 8;   // packed bytes per W row per step
   static constexpr int A_TILE = BM * BK * 2;                    // 32 KB
@@ -474,20 +475,32 @@ __global__ __launch_bounds__(512) void k_gemm8(const uint16_t* __restrict__ x, i
     const uint8_t* Bn = lds + st1 * C::STAGE + C::A_TILE;
     u32x4_t wc[NJ];
     wchunk(Bn, wc);
-#pragma unroll
-    for (int s4 = 0; s4 < 4; s4++) {
-      bf16x8_t af[MI];
+    auto load_a = [&](int s4, bf16x8_t (&dst)[MI]) {
 #pragma unroll
       for (int i = 0; i < MI; i++) {
         const int r = wm * C::TM + 32 * i + l32;
-        af[i] = as_bf16x8(ld16(A + r * 128 + (((4 * h + s4) ^ aswz(r)) << 4)));
+        dst[i] = as_bf16x8(ld16(A + r * 128 + (((4 * h + s4) ^ aswz(r)) << 4)));
       }
+    };
+    // PF: the x fragments of slice s4 + 1 are read during slice s4
+    constexpr bool PF = C::PREFETCH_A;
+    bf16x8_t af[PF ? 2 : 1][MI];
+    if constexpr (PF) load_a(0, af[0]);
+#pragma unroll
+    for (int s4 = 0; s4 < 4; s4++) {
+      if constexpr (PF) {
+        if (s4 < 3) load_a(s4 + 1, af[(s4 + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        load_a(s4, af[0]);
+      }
+      const int cur = PF ? (s4 & 1) : 0;
       dequant_q(Bn, wc, s4, cn, bnext);
 #pragma unroll
       for (int i = 0; i < MI; i++)
 #pragma unroll
         for (int j = 0; j < NJ; j++)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bcur[s4][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bcur[s4][j], acc[i][j], 0, 0, 0);
     }
     // group kt + 2 complete: with four stages the loads queued behind it are
     // the scales of group kt + 1, group kt + 3 and the scales of group kt + 2
