@@ -601,6 +601,15 @@ hipError_t cu_count(int* n) {
 // refill never targets the slot the current step reads.
 __host__ __device__ constexpr int ring_slots(int spw, int r) { return r < spw ? r + 1 : r; }
 
+// E4M3 weights bypass the LDS ring: every step of the slice is loaded into
+// registers up front (measured faster for 1-3 tokens, where the conversion is
+// cheap; for INT4 the conversions then bunch behind the last arrivals and the
+// ring is faster).
+template <int WDT>
+__host__ __device__ constexpr bool ring_regw(bool xs) {
+  return WDT == W_FP8 && !xs;
+}
+
 // Per-wave LDS of a ring tile (bytes): the ring, the x rows (the whole slice,
 // or with XS a 4-token x chunk in every slot) and the slice's scales.
 template <int WDT, int GSH>
@@ -611,7 +620,7 @@ __host__ __device__ constexpr int ring_wave_bytes(int spwe, int r, bool half, bo
   const int sbrow = (ksl >> gshift_of<WDT>(GSH)) * scale_bytes<WDT>();
   const int sbytes = WDT == W_FP8 ? 0 : 16 * (sbrow < 16 ? 16 : sbrow);
   const int ns = ring_slots(spwe, r);
-  const int ring = xs ? ns * (1024 + xr * 4 * kstep * 2) : ns * 1024 + xr * m * ksl * 2;
+  const int ring = xs ? ns * (1024 + xr * 4 * kstep * 2) : (ring_regw<WDT>(xs) ? 0 : ns * 1024) + xr * m * ksl * 2;
   return ring + ((sbytes + 15) & ~15);
 }
 
@@ -688,8 +697,9 @@ __device__ __forceinline__ void gemv_ring_tile(const uint16_t* __restrict__ x, i
   constexpr int SLOT = XS ? 1024 + XR * XCH : 1024;
   constexpr int VMS = XS ? 1 + XR : 1;                        // loads per step
   const int wstride = ring_wave_bytes<WDT, GSH>(SPWE, R, HALF, XS, M);
+  constexpr bool REGW = ring_regw<WDT>(XS);
   uint8_t* ring = smem + wave * wstride;
-  uint8_t* xl = ring + NS * SLOT;
+  uint8_t* xl = ring + (REGW ? 0 : NS * SLOT);
   uint8_t* sl = xl + (XS ? 0 : XR * M * XROW);
 
   // 1) scales of the slice.  When a row of the slice holds >= 16 bytes of
@@ -735,9 +745,11 @@ __device__ __forceinline__ void gemv_ring_tile(const uint16_t* __restrict__ x, i
   constexpr int XCPR = XRB / 16;                              // 16-byte chunks per x row of a step
   const int xtok = lane / XCPR;
   const uint32_t xlane = (uint32_t)(xtok * (uint32_t)K + kbase + 8 * (lane % XCPR)) * 2;
+  u32x4_t wreg[REGW ? SPWE : 1];
   auto issue_step = [&](int slot, int c) {
     uint8_t* sp = ring + slot * SLOT;
-    lds_dma16(rw, sp, wlane, c * KSTEP * BPE2 / 2);
+    if constexpr (REGW) wreg[c] = bld16(rw, wlane + c * KSTEP * BPE2 / 2);
+    else lds_dma16(rw, sp, wlane, c * KSTEP * BPE2 / 2);
     if constexpr (XS) {
 #pragma unroll
       for (int h = 0; h < XR; h++)
@@ -745,7 +757,7 @@ __device__ __forceinline__ void gemv_ring_tile(const uint16_t* __restrict__ x, i
     }
   };
 #pragma unroll
-  for (int c = 0; c < R; c++) issue_step(c, c);
+  for (int c = 0; c < (REGW ? SPWE : R); c++) issue_step(c, c);
 
   f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int tok = HALF ? (nl & 7) : nl;                       // token of this lane's x operand row
@@ -755,15 +767,15 @@ __device__ __forceinline__ void gemv_ring_tile(const uint16_t* __restrict__ x, i
   for (int c = 0; c < SPWE; c++) {
     // step loads issued after step c's: min(R-1, SPWE-1-c) steps of VMS loads
     // (each step issues its refill after this wait)
-    wait_vm_n((c + R - 1 < SPWE ? R - 1 : SPWE - 1 - c) * VMS);
-    if (c + R < SPWE) {
+    wait_vm_n(REGW ? SPWE - 1 - c : (c + R - 1 < SPWE ? R - 1 : SPWE - 1 - c) * VMS);
+    if (!REGW && c + R < SPWE) {
       // step c + R goes to the slot step c - 1 read: that read returned before
       // step c - 1's conversion, and nothing may be scheduled across the
       // barrier (a DMA write is not ordered after an earlier LDS read)
       __builtin_amdgcn_sched_barrier(0);
       issue_step((c + R) % NS, c + R);
     }
-    const u32x4_t wv = *reinterpret_cast<const u32x4_t*>(ring + (c % NS) * SLOT + lane * 16);
+    const u32x4_t wv = REGW ? wreg[c] : *reinterpret_cast<const u32x4_t*>(ring + (c % NS) * SLOT + lane * 16);
     scale_t<WDT> scv{};
     if constexpr (WDT == W_INT4) {
       const uint32_t gi = (uint32_t)(c * KSTEP + EPL * g) >> gs;
@@ -1017,7 +1029,9 @@ wq_status ring_launch(int64_t M, const uint16_t* x, int64_t N, int64_t K, const 
                       const float* ch, float alpha, uint16_t* y, hipStream_t s) {
   const int full = ring_wave_bytes<WDT, GSH>(SPW, R, false, XS, (int)M);
   const int half = SPW >= 2 ? ring_wave_bytes<WDT, GSH>(SPW / 2, ring_half_depth(SPW, R, XS), true, XS, (int)M) : 0;
-  const size_t lds = (size_t)RING_NW * (full > half ? full : half);
+  // at least the split-K reduction's 16 x 16 fp32 partials per wave
+  const int wave_bytes = full > half ? full : half;
+  const size_t lds = (size_t)RING_NW * (wave_bytes > 1024 ? wave_bytes : 1024);
   if (allow_lds<k_gemv_ring<WDT, SPW, R, RING_NW, GSH, XS>>(lds) != hipSuccess) return WQ_EHIP;
   // all tiles are resident at once and dispatched round by round over the
   // CUs; a last round that covers at most half of the CUs becomes twice as
