@@ -215,6 +215,23 @@ def test_gemv_int4_offset_activations(W, M):
     _check(W.wq_gemm(dev_bf16(xbits), *args, N), xbits, wdeq, chan)
 
 
+@pytest.mark.parametrize("kind", ["int4", "mxfp4", "e4m3"])
+@pytest.mark.parametrize("M", [5, 8, 13, 16])
+@pytest.mark.parametrize("N,K", [(300, 2048), (1000, 4096), (64, 4096)])
+def test_gemv_x_once_per_workgroup(W, kind, M, N, K):
+    # 5 <= M <= 16 with K = 2048 or 4096 takes the form that stages x in LDS
+    # once per workgroup of 64 columns: ragged last workgroup (300 = 4 x 64 +
+    # 44, 1000 = 15 x 64 + 40), a single workgroup, every M that leaves MFMA
+    # rows without a token
+    g = np.random.default_rng(900 + M * 3 + N + K)
+    Wf = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
+    Wf[:, g.choice(K, 5, replace=False)] *= 30
+    xbits = to_bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    args, wdeq, chan = _prep(W, kind, Wf)
+    banner("gemv x once per workgroup", kind, M, N, K)
+    _check(W.wq_gemm(dev_bf16(xbits), *args, N), xbits, wdeq, chan)
+
+
 @pytest.mark.parametrize("kind", ["int4", "mxfp4"])
 @pytest.mark.parametrize("M,N", [(1, 300), (4, 272)])
 def test_gemv_long_k(W, kind, M, N):

@@ -999,6 +999,135 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_ring16(const uint16_t* __restr
   }
 }
 
+// Decode GEMV for 4 < M <= 16, x once per workgroup: every workgroup of the
+// ring form reads the whole x (M x K bf16) from L2, as many times as there are
+// workgroups, which is more bytes than the weights themselves at M = 16.  Here
+// one workgroup of WW waves owns CTW column tiles (16 W rows each) over all of
+// K, wave w the K slice [w*KSL, (w+1)*KSL) of SPW steps, so x crosses from L2
+// once per workgroup (about once per CU).  Each wave stages the x rows of its
+// own slice in a private LDS region by direct-to-LDS loads of whole rows of
+// the slice, each row's 16-byte chunks XOR-swizzled by the row so that the 16
+// rows of one fragment read sit in distinct banks (x loaded straight into
+// registers in the MFMA layout touches two cache lines per row and load: 1 us
+// slower at M = 16, no faster at M = 5).  Each lane loads the scales and weight
+// chunks of all its steps and tiles into registers up front; the steps then
+// convert and multiply in order as the loads land.  The wave partials meet in
+// LDS, over the consumed x rows.
+template <int WDT, int SPW, int WW, int CTW, int GSH>
+__global__ __launch_bounds__(64 * WW) __attribute__((amdgpu_waves_per_eu(WW / 4, WW / 4))) void k_gemv_wide(
+    const uint16_t* __restrict__ x, int M, int64_t N, int64_t K, const uint8_t* __restrict__ w,
+    const void* __restrict__ sc, const float* __restrict__ chscale, float alpha, uint16_t* __restrict__ y) {
+  constexpr int EPL = WTraits<WDT>::bits == 4 ? 32 : 16;
+  constexpr int KSTEP = 4 * EPL;
+  constexpr int KSL = SPW * KSTEP;
+  constexpr int MF = EPL / 8;
+  constexpr int BPE2 = WTraits<WDT>::bits == 4 ? 1 : 2;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nl = lane & 15, g = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * 16 * CTW;
+  const uint32_t rowbytes = (uint32_t)(K * BPE2 / 2);
+  const int64_t nrows = N - n0 < 16 * CTW ? N - n0 : 16 * CTW;
+  constexpr int gs = gshift_of<WDT>(GSH);
+  const uint32_t spr = (uint32_t)(K >> gs);
+  constexpr int SB = scale_bytes<WDT>();
+  const auto rw = make_rsrc(w + n0 * rowbytes, nrows * rowbytes);
+  const auto rs = make_rsrc(reinterpret_cast<const uint8_t*>(sc) + (WDT == W_FP8 ? 0 : n0 * spr * SB),
+                            WDT == W_FP8 ? 0 : nrows * spr * SB);
+  const auto rx = make_rsrc(x, (int64_t)M * K * 2);
+  const uint32_t kbase = (uint32_t)(wave * KSL);
+
+  // 1) the x rows of the wave's slice (XRB bytes each) at row * XRB of the
+  //    wave's region; 16-byte slot p of row r holds the slice's chunk
+  //    p ^ (r & 15).  One DMA instruction moves RPD rows.
+  constexpr int XRB = KSL * 2, RPD = 1024 / XRB, CPRW = XRB / 16;
+  static_assert(XRB <= 1024 && CPRW >= 16, "x slice rows of 256 to 1024 bytes");
+  uint8_t* xw = smem + wave * 16 * XRB;
+  {
+    const int rl = lane / CPRW, p = lane % CPRW;
+    for (int i = 0; i * RPD < M; i++) {
+      const int r = i * RPD + rl;
+      if (r < M) lds_dma16(rx, xw + i * 1024, (uint32_t)(r * (uint32_t)K + kbase) * 2 + 16 * (p ^ (r & 15)));
+    }
+  }
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2) scales and weight chunks of every step into registers, the scales first
+  //    (needed by the first conversion); the scheduling barriers keep every
+  //    load ahead of the first conversion (the scheduler would otherwise sink
+  //    later steps' loads to save registers)
+  u32x4_t wr[SPW][CTW];
+  uint32_t svr[SPW][CTW];
+  const uint32_t wlane = (uint32_t)nl * rowbytes + (kbase + EPL * g) * BPE2 / 2;
+  if constexpr (WDT != W_FP8) {
+#pragma unroll
+    for (int c = 0; c < SPW; c++)
+#pragma unroll
+      for (int t = 0; t < CTW; t++)
+        svr[c][t] = scale_raw_of<WDT>(rs, (uint32_t)(16 * t + nl) * spr + ((kbase + c * KSTEP + EPL * g) >> gs));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int c = 0; c < SPW; c++)
+#pragma unroll
+    for (int t = 0; t < CTW; t++) wr[c][t] = bld16(rw, wlane + 16 * t * rowbytes + c * KSTEP * BPE2 / 2);
+  __builtin_amdgcn_sched_barrier(0);
+  // this wave's x rows have landed once only the register loads issued after
+  // them remain (LDS accesses of one wave execute in order: no barrier)
+  wait_vm<SPW * CTW * (WDT == W_FP8 ? 1 : 2)>();
+  // MFMA rows >= M read row 0 (their outputs are discarded)
+  const int xtr = nl < M ? nl : 0;
+  const uint8_t* xrow = xw + xtr * XRB;
+
+  f32x4_t acc[CTW];
+#pragma unroll
+  for (int t = 0; t < CTW; t++) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < SPW; c++) {
+    bf16x8_t xa[MF];
+#pragma unroll
+    for (int j = 0; j < MF; j++) {
+      const uint32_t q = (c * KSTEP + EPL * g + 8 * j) / 8;
+      xa[j] = as_bf16x8(ld16(xrow + 16 * (q ^ (uint32_t)(xtr & 15))));
+    }
+#pragma unroll
+    for (int t = 0; t < CTW; t++) {
+      bf16x8_t bq[4];
+      dequant16<WDT>(wr[c][t], scale_from_raw<WDT>(WDT == W_FP8 ? 0u : svr[c][t]), bq);
+#pragma unroll
+      for (int j = 0; j < MF; j++) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[j], bq[j], acc[t], 0, 0, 0);
+    }
+  }
+
+  // acc[t][i] holds C[m = 4g + i][n = nl] of column tile t; the WW wave
+  // partials of every output are added in LDS (over the x rows, once every
+  // wave is done with them), one output per thread.  The scheduling barrier
+  // keeps the register-only MFMA work ahead of the workgroup barrier (the
+  // scheduler may otherwise move it past, and every wave then waits there for
+  // the slowest one's loads)
+  float* red = reinterpret_cast<float*>(smem);
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < CTW; t++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) red[((wave * CTW + t) * 16 + 4 * g + i) * 16 + nl] = acc[t][i];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < CTW * 256; idx += 64 * WW) {
+    const int t = idx >> 8, m = (idx >> 4) & 15, n = idx & 15;
+    const int64_t col = n0 + 16 * t + n;
+    if (m < M && col < N) {
+      float v = 0.0f;
+#pragma unroll
+      for (int wv = 0; wv < WW; wv++) v += red[((wv * CTW + t) * 16 + m) * 16 + n];
+      v *= WDT == W_FP8 ? chscale[col] * alpha : alpha;
+      y[(int64_t)m * N + col] = (uint16_t)f32_to_bf16_bits(v);
+    }
+  }
+}
+
 // Measured on MI355X for K = 4096: 4 waves per 16-column tile with a 2-deep
 // ring beat deeper rings (requests all in flight arrive in an order that
 // bunches the dequantization work at the end) and 8-wave splits.
@@ -1006,7 +1135,7 @@ constexpr int RING_NW = 4;
 constexpr int RING_DEPTH = 2;
 // 4 < M <= 16: two 16-column tiles per workgroup share every x chunk, which
 // halves the x traffic from L2 (each workgroup reads the whole x slice).
-constexpr int RING16_CT = 2;
+constexpr int RING16_CT = 2, RING16_NW = 4;
 template <int WDT, int SPW, int GSH>
 wq_status ring16_go(int64_t M, const uint16_t* x, int64_t N, int64_t K, const uint8_t* w, const void* sc,
                     const float* ch, float alpha, uint16_t* y, hipStream_t s) {
@@ -1016,12 +1145,29 @@ wq_status ring16_go(int64_t M, const uint16_t* x, int64_t N, int64_t K, const ui
   } else {
     constexpr int CT = RING16_CT;
     constexpr int XSLOT = 16 * 4 * (WTraits<WDT>::bits == 4 ? 32 : 16) * 2;
-    const size_t lds = (size_t)RING_NW * R * (CT * 1024 + XSLOT);
+    constexpr int NW = RING16_NW;
+    const size_t lds = (size_t)NW * R * (CT * 1024 + XSLOT);
     const unsigned grid = (unsigned)((N + 16 * CT - 1) / (16 * CT));
-    if (allow_lds<k_gemv_ring16<WDT, SPW, R, RING_NW, CT, GSH>>(lds) != hipSuccess) return WQ_EHIP;
-    k_gemv_ring16<WDT, SPW, R, RING_NW, CT, GSH><<<grid, 64 * RING_NW, lds, s>>>(x, (int)M, N, K, w, sc, ch, alpha, y);
+    if (allow_lds<k_gemv_ring16<WDT, SPW, R, NW, CT, GSH>>(lds) != hipSuccess) return WQ_EHIP;
+    k_gemv_ring16<WDT, SPW, R, NW, CT, GSH><<<grid, 64 * NW, lds, s>>>(x, (int)M, N, K, w, sc, ch, alpha, y);
     return WQ_OK;
   }
+}
+
+// x-once form: 16 waves x 4 column tiles per workgroup, K = 2048 or 4096
+// (1 or 2 steps per wave for 4-bit weights, 2 or 4 for E4M3)
+constexpr int WIDE_WW = 16, WIDE_CTW = 4;
+template <int WDT, int SPW, int GSH>
+wq_status wide_go(int64_t M, const uint16_t* x, int64_t N, int64_t K, const uint8_t* w, const void* sc,
+                  const float* ch, float alpha, uint16_t* y, hipStream_t s) {
+  // x: 16 rows of the wave's slice per wave (K * 2 * 16 bytes in all); the
+  // partials reuse it
+  const size_t red = (size_t)WIDE_WW * WIDE_CTW * 1024, xb = (size_t)16 * K * 2;
+  const size_t lds = xb > red ? xb : red;
+  const unsigned grid = (unsigned)((N + 16 * WIDE_CTW - 1) / (16 * WIDE_CTW));
+  if (allow_lds<k_gemv_wide<WDT, SPW, WIDE_WW, WIDE_CTW, GSH>>(lds) != hipSuccess) return WQ_EHIP;
+  k_gemv_wide<WDT, SPW, WIDE_WW, WIDE_CTW, GSH><<<grid, 64 * WIDE_WW, lds, s>>>(x, (int)M, N, K, w, sc, ch, alpha, y);
+  return WQ_OK;
 }
 
 template <int WDT, int SPW, int R, int GSH, bool XS>
@@ -1082,7 +1228,11 @@ bool ring_path(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t
       default: return false;
     }
   }
-  switch (spw) {
+  constexpr int SW = WTraits<WDT>::bits == 4 ? 1 : 2;          // steps per wave at K = 2048
+  if (K == 2048) { st = wide_go<WDT, SW, GSH>(M, x, N, K, w, sc, ch, alpha, y, s); return true; }
+  if (K == 4096) { st = wide_go<WDT, 2 * SW, GSH>(M, x, N, K, w, sc, ch, alpha, y, s); return true; }
+  if (K % (KSTEP * RING16_NW)) return false;
+  switch (K / (KSTEP * RING16_NW)) {
     case 2: st = ring16_go<WDT, 2, GSH>(M, x, N, K, w, sc, ch, alpha, y, s); return true;
     case 4: st = ring16_go<WDT, 4, GSH>(M, x, N, K, w, sc, ch, alpha, y, s); return true;
     case 8: st = ring16_go<WDT, 8, GSH>(M, x, N, K, w, sc, ch, alpha, y, s); return true;
