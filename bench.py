@@ -25,7 +25,7 @@ torch.matmul (hipBLASLt) at the prefill shape as secondary denominators.
 
 --only CASE runs a single case without the full summary (for rocprofv3):
 decode (the same graph-timed steps as the headline, prints one short JSON
-line), decode_w8, decode_nvfp4, decode_asym, prefill, prefill_nvfp4, w8a8_block, w8a8_channel, quant_e4m3, quant_mxfp4, quant_mxfp8, wquant_mxfp4, copy,
+line), decode_m4, decode_m16, decode_w8, decode_nvfp4, decode_asym, prefill, prefill_nvfp4, w8a8_block, w8a8_channel, quant_e4m3, quant_mxfp4, quant_mxfp8, wquant_mxfp4, copy,
 moe_gate_up, moe_down.
 """
 from __future__ import annotations
@@ -367,7 +367,7 @@ class Copy:
 # CPU baseline: the oracle on a bounded sample of the decode workload
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(rows=4096, reps=3):
+def cpu_baseline(rows=14336, reps=3):
     from threadpoolctl import threadpool_limits
     from oracle import dequant as OD
     from oracle import gemm as OG
@@ -378,18 +378,30 @@ def cpu_baseline(rows=4096, reps=3):
     packed, sb, _ = OI.quantize_int4(Wf, 128)          # weight preparation, not timed
     K = Wf.shape[1]
     nbytes = packed.nbytes + sb.nbytes + K * 2 + rows * 2
-    times = []
-    with threadpool_limits(limits=1):
-        for _ in range(reps):
-            t = time.perf_counter()
-            wd = OD.dequant_int4(packed, sb, 128)
-            y, _ = OG.reference(xbits, wd)
-            times.append(time.perf_counter() - t)
-    t = float(np.median(times))
-    return {"value": nbytes / t / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"decode W4A16 M=1 K=4096 on the first {rows} of 14336 output rows "
-                      f"(INT4 dequant + fp64 matvec), median of {reps}, single-threaded",
-            "seconds_per_sample_step": t}
+    ncores = len(os.sched_getaffinity(0))
+
+    def timed(threads):
+        times = []
+        with threadpool_limits(limits=threads):
+            for _ in range(reps):
+                t = time.perf_counter()
+                wd = OD.dequant_int4(packed, sb, 128)
+                OG.reference(xbits, wd)
+                times.append(time.perf_counter() - t)
+        return float(np.median(times))
+
+    t1 = timed(1)
+    tn = timed(ncores)
+    # the reported figure is the faster of the two thread counts
+    best, cores = (tn, ncores) if tn < t1 else (t1, 1)
+    return {"value": nbytes / best / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"decode W4A16 M=1 K=4096 on {rows} of the 14336 output rows "
+                      f"(INT4 dequant in NumPy, fp64 matvec through BLAS), median of {reps}; BLAS threads 1 and "
+                      f"{ncores} (all cores in the affinity mask) both timed",
+            "seconds_per_sample_step": best,
+            "by_threads": {"1": {"GB/s": nbytes / t1 / 1e9, "s": t1},
+                           str(ncores): {"GB/s": nbytes / tn / 1e9, "s": tn}},
+            "os_cpu_count": os.cpu_count(), "affinity_cores": ncores}
 
 
 # ---------------------------------------------------------------------------
@@ -408,6 +420,7 @@ def main():
     if args.only and args.only != "decode":
         case = args.only
         mk = {"decode_w8": lambda: Decode(torch, W, 1, "e4m3"), "decode_nvfp4": lambda: Decode(torch, W, 1, "nvfp4"),
+              "decode_m16": lambda: Decode(torch, W, 16), "decode_m4": lambda: Decode(torch, W, 4),
               "decode_asym": lambda: Decode(torch, W, 1, "int4_asym"),
               "prefill_nvfp4": lambda: Prefill(torch, W, kind="nvfp4"),
               "w8a8_block": lambda: W8A8(torch, W, "block"), "w8a8_channel": lambda: W8A8(torch, W, "channel"),
@@ -417,9 +430,11 @@ def main():
               "wquant_mxfp4": lambda: WeightQuant(torch, W),
               "moe_gate_up": lambda: MoeW4A8(torch, W, "gate_up"), "moe_down": lambda: MoeW4A8(torch, W, "down")}[case]
         obj = mk()
-        reps = args.reps or (10 if case in ("prefill", "prefill_nvfp4", "moe_gate_up", "moe_down", "w8a8_block",
-                                            "w8a8_channel") else 100)
-        for i in range(reps):
+        big = case in ("prefill", "prefill_nvfp4", "moe_gate_up", "moe_down", "w8a8_block", "w8a8_channel")
+        reps = args.reps or (20 if big else 100)
+        # the clocks settle over the first launches of a large kernel: the
+        # profile's median then reflects the steady state, as the timed runs do
+        for i in range(reps + (3 if big else 0)):
             obj.launch(i)
         torch.cuda.synchronize()
         print(f"{case}: {reps} launches done", flush=True)
