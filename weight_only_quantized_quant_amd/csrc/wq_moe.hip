@@ -218,8 +218,14 @@ constexpr int MB_TILE = MBN * MBK / 2;                  // 16 KB of packed INT4
 constexpr int MSTAGE = MA_TILE + MB_TILE;
 constexpr int MNSTAGE = 3;                              // loads run two steps ahead
 constexpr int MLDS = MNSTAGE * MSTAGE;                  // 144 KB
-// W rows of 64 bytes: chunk c of row r sits at c ^ ((r >> 1) & 3)
-__device__ __forceinline__ int mbswz(int r) { return (r >> 1) & 3; }
+// LDS placement of the tiles' 16-byte chunks.  A ds_read_b128 serves 16
+// lanes per pass over 64 banks (256 bytes), so the 16 rows one fragment read
+// touches must land on distinct 16-byte bank groups.  Activation rows of 128
+// bytes (two rows per 256 bytes): chunk c of row r at c ^ ((r >> 1) & 7).  W
+// rows of 64 bytes (four rows per 256 bytes): chunk c of row r at
+// c ^ ((r >> 2) & 3).
+__device__ __forceinline__ int maswz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int mbswz(int r) { return (r >> 2) & 3; }
 // The 8 waves all lie along N, each owning 256 rows x 32 channels (8 MFMA
 // tiles of 32x32): every W fragment is converted through its table once per
 // workgroup (with 2 x 4 waves the two M-halves converted each fragment twice),
@@ -289,7 +295,7 @@ __global__ __launch_bounds__(512) void k_moe_gemm(const uint8_t* __restrict__ x8
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     const int r = 8 * (wave * 4 + i) + (lane >> 3);
-    const int c = (lane & 7) ^ (r & 7);
+    const int c = (lane & 7) ^ maswz(r);
     const int64_t gr = r0 + r;
     if (gr < r1) {
       const int64_t tok = row_token ? row_token[gr] : gr;
@@ -338,8 +344,8 @@ __global__ __launch_bounds__(512) void k_moe_gemm(const uint8_t* __restrict__ x8
   auto load_a = [&](const uint8_t* A, int s2, int i) -> i32x8_t {
     const int r = 32 * i + l32;
     const int c0 = 4 * s2 + 2 * h;
-    const u32x4_t p0 = ld16(A + r * 128 + ((c0 ^ (r & 7)) << 4));
-    const u32x4_t p1 = ld16(A + r * 128 + (((c0 + 1) ^ (r & 7)) << 4));
+    const u32x4_t p0 = ld16(A + r * 128 + ((c0 ^ maswz(r)) << 4));
+    const u32x4_t p1 = ld16(A + r * 128 + (((c0 + 1) ^ maswz(r)) << 4));
     return i32x8_t{(int)p0[0], (int)p0[1], (int)p0[2], (int)p0[3], (int)p1[0], (int)p1[1], (int)p1[2], (int)p1[3]};
   };
   // the 8 MFMAs of half s2; tile i + 1's operand is read while tile i's MFMA runs
