@@ -22,6 +22,9 @@ MXFP4 weight quantizer, the W8A8 FP8 GEMM at the prefill shape (block-scaled
 and per-token x per-channel), the W4A8 mixture-of-experts grouped GEMMs (gate/up and
 down, with routing, token quantization and prepack), a streaming copy and
 torch.matmul (hipBLASLt) at the prefill shape as secondary denominators.
+`gpu_clocks_hwmon` holds SCLK, MCLK and board power sampled from the GPU's
+sysfs files during the decode timed region and the prefill timed rounds (left
+out where sysfs does not expose them).
 
 --only CASE runs a single case without the full summary (for rocprofv3):
 decode (the same graph-timed steps as the headline, prints one short JSON
@@ -94,6 +97,74 @@ def time_graph(torch, g, launches):
     b.synchronize()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / launches
+
+
+class ClockSampler:
+    """SCLK, MCLK and board power of the GPU, read from its sysfs files (hwmon,
+    else the current level of pp_dpm_sclk / pp_dpm_mclk) on a background
+    thread while a timed region runs.  Keys whose files are missing or
+    unreadable are left out."""
+
+    FILES = (("sclk_mhz", "freq1_input", 1e-6), ("mclk_mhz", "freq2_input", 1e-6),     # Hz, microwatts
+             ("power_w", "power1_average", 1e-6), ("power_w", "power1_input", 1e-6))
+
+    def __init__(self, torch):
+        import threading
+        self.files, self.samples = {}, {}
+        self.stop_evt, self.thread = threading.Event(), None
+        try:
+            p = torch.cuda.get_device_properties(0)
+            dev = f"/sys/bus/pci/devices/{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}.0"
+            for h in sorted(os.listdir(os.path.join(dev, "hwmon"))):
+                for key, fn, scale in self.FILES:
+                    f = os.path.join(dev, "hwmon", h, fn)
+                    if key not in self.files and os.access(f, os.R_OK):
+                        self.files[key] = (f, scale)
+            for key, fn in (("sclk_mhz", "pp_dpm_sclk"), ("mclk_mhz", "pp_dpm_mclk")):
+                f = os.path.join(dev, fn)
+                if key not in self.files and os.access(f, os.R_OK):
+                    self.files[key] = (f, None)
+        except (OSError, AttributeError):
+            pass
+
+    @staticmethod
+    def _value(text, scale):
+        if scale is not None:
+            return int(text.strip()) * scale
+        for line in text.splitlines():                  # "1: 2400Mhz *" marks the current level
+            if line.rstrip().endswith("*"):
+                return float(line.split(":")[1].strip().split()[0].lower().replace("mhz", ""))
+        raise ValueError("no current level")
+
+    def _run(self):
+        while not self.stop_evt.is_set():
+            for key, (f, scale) in self.files.items():
+                try:
+                    with open(f) as fh:
+                        self.samples.setdefault(key, []).append(self._value(fh.read(), scale))
+                except (OSError, ValueError, IndexError):
+                    pass
+            self.stop_evt.wait(0.0005)
+
+    def __enter__(self):
+        import threading
+        self.samples = {}
+        self.stop_evt.clear()
+        if self.files:
+            self.thread = threading.Thread(target=self._run, daemon=True)
+            self.thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop_evt.set()
+        if self.thread is not None:
+            self.thread.join()
+            self.thread = None
+        return False
+
+    def summary(self):
+        return {k: {"median": round(float(np.median(v)), 1), "max": round(float(np.max(v)), 1), "samples": len(v)}
+                for k, v in self.samples.items() if v} or None
 
 
 def time_eager(torch, fn, reps, warm=3, rounds=3):
@@ -445,9 +516,12 @@ def main():
     timed_g = graph_of(torch, [lambda i=i: dec.launch(i) for i in range(K)])
     warm_g.replay()
     torch.cuda.synchronize()
+    clocks = ClockSampler(torch)
     t0 = time.perf_counter()
-    ms = time_graph(torch, timed_g, K)
+    with clocks:
+        ms = time_graph(torch, timed_g, K)
     wall = time.perf_counter() - t0
+    clock_summary = {"decode_timed_region": clocks.summary()}
     value = dec.bytes / (ms * 1e-3) / 1e9
     traffic = stored_traffic("decode_w4a16_m1", dec.bytes)
     roofline = {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -480,7 +554,9 @@ def main():
     torch.cuda.empty_cache()
 
     pf = Prefill(torch, W)
-    t = time_eager(torch, pf.launch, 10)
+    with clocks:
+        t = time_eager(torch, pf.launch, 10)
+    clock_summary["prefill_mxfp4_timed_rounds"] = clocks.summary()
     tf = pf.flops / (t * 1e-3) / 1e12
     secondary["prefill_mxfp4_m8192"] = {"TFLOP/s": round(tf, 1), "frac_bf16_mfma": round(tf / BF16_PEAK_TFLOPS, 4),
                                         "ms": round(t, 3), "flops": pf.flops}
@@ -559,6 +635,7 @@ def main():
                                "per 128-element group; bf16 x with 0.5% channels x30; weights cycled over "
                                f"{len(dec.copies)} resident copies", "parallelism": "none (1 GPU)"},
         "roofline": roofline, "cpu_baseline": cpu, "secondary": secondary,
+        "gpu_clocks_hwmon": clock_summary,
         "wall_s_timed_region": round(wall, 4),
     }
     print(json.dumps(line), flush=True)
