@@ -1,10 +1,12 @@
 // Weight-only quantized matmul y[M,N] = x[M,K] . dequant(W[N,K])^T for gfx950.
 //
-// Decode (M <= 16): split-K GEMV.  A workgroup owns 16 output columns; its
-// waves split K, stream the packed weights (through a small LDS ring fed by
-// direct-to-LDS loads when M <= 4), convert them to bf16 in registers and feed
-// v_mfma_f32_16x16x32_bf16 with the x rows as the other operand.  The partial
-// 16x16 tiles are reduced through LDS and rounded to bf16 once.
+// Decode (M <= 16): split-K GEMV.  For M <= 4 a workgroup of 4 waves owns 16
+// output columns; its waves split K and stream the packed weights through a
+// small LDS ring fed by direct-to-LDS loads (E4M3 weights straight into
+// registers).  For 4 < M <= 16 a workgroup of 16 waves owns 64 columns and
+// stages x once in LDS.  The weights are converted to bf16 in registers and
+// feed v_mfma_f32_16x16x32_bf16 with the x rows as the other operand; the
+// partial 16x16 tiles are reduced through LDS and rounded to bf16 once.
 //
 // Prefill (M > 16): 256x256 output tile per workgroup of 8 waves, K step 64,
 // three LDS stages filled by direct-to-LDS loads (x in bf16, W still packed);
