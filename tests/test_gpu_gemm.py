@@ -216,6 +216,22 @@ def test_gemv_int4_offset_activations(W, M):
 
 
 @pytest.mark.parametrize("kind", ["int4", "mxfp4", "e4m3"])
+@pytest.mark.parametrize("M", [1, 4, 16])
+@pytest.mark.parametrize("N,K", [(100, 11008), (70, 14336), (90, 640)])
+def test_gemv_uneven_k_split(W, kind, M, N, K):
+    # K whose step count the ring forms do not take (86, 112 or 5 steps of
+    # 128 for 4-bit weights): the general GEMV splits the steps over up to 8
+    # waves with shares differing by one chunk
+    g = np.random.default_rng(1100 + M * 5 + N + K)
+    Wf = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
+    Wf[:, g.choice(K, 4, replace=False)] *= 25
+    xbits = to_bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    args, wdeq, chan = _prep(W, kind, Wf)
+    banner("gemv uneven K split", kind, M, N, K)
+    _check(W.wq_gemm(dev_bf16(xbits), *args, N), xbits, wdeq, chan)
+
+
+@pytest.mark.parametrize("kind", ["int4", "mxfp4", "e4m3"])
 @pytest.mark.parametrize("M", [5, 8, 13, 16])
 @pytest.mark.parametrize("N,K", [(300, 2048), (1000, 4096), (64, 4096)])
 def test_gemv_x_once_per_workgroup(W, kind, M, N, K):

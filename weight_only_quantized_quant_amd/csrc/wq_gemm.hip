@@ -134,11 +134,14 @@ __device__ __forceinline__ scale_t<WDT> scale_of(__amdgpu_buffer_rsrc_t r, uint3
 // No workgroup barrier is needed: LDS operations of one wave execute in order.
 // Otherwise x is read with buffer loads (rows >= M read as zeros).
 // Issue order per chunk: x staging loads, scales, weights.
+// K splits into nchunk chunks of NSTEP steps; wave w of the S waves takes
+// chunks [w nchunk / S, (w + 1) nchunk / S), so the waves' shares differ by at
+// most one chunk whatever K is.
 template <int WDT, int TN, int NSTEP, bool XLDS>
 __global__ __launch_bounds__(512) void k_gemv(const uint16_t* __restrict__ x, int M, int64_t N, int64_t K,
                                              const uint8_t* __restrict__ w, const void* __restrict__ sc,
                                              int group_shift, const float* __restrict__ chscale, float alpha,
-                                             uint16_t* __restrict__ y, int niter) {
+                                             uint16_t* __restrict__ y, int nchunk) {
   constexpr int EPL = WTraits<WDT>::bits == 4 ? 32 : 16;   // elements per lane per step
   constexpr int KSTEP = 4 * EPL;                            // K covered by a wave per step
   constexpr int KCH = NSTEP * KSTEP;                        // K per wave per chunk
@@ -161,7 +164,8 @@ __global__ __launch_bounds__(512) void k_gemv(const uint16_t* __restrict__ x, in
   const auto rs = make_rsrc(reinterpret_cast<const uint8_t*>(sc) + (WDT == W_FP8 ? 0 : n0 * spr * SB),
                             WDT == W_FP8 ? 0 : nrows * spr * SB);
   const auto rx = make_rsrc(x, (int64_t)M * K * 2);
-  const uint32_t kbase = (uint32_t)(wave * niter * KCH);
+  const int c0 = (int)((int64_t)wave * nchunk / S), niter = (int)((int64_t)(wave + 1) * nchunk / S) - c0;
+  const uint32_t kbase = (uint32_t)(c0 * KCH);
 
   uint8_t* xw = smem + wave * XW;                            // this wave's x rows, then zeros
   float* red = reinterpret_cast<float*>(smem + (XLDS ? S * XW : 0));
@@ -848,16 +852,15 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_ring(const uint16_t* __restric
   gemv_ring_tile<WDT, SPW, R, NW, GSH, false, XS>(x, M, N, K, w, sc, chscale, alpha, y, (int64_t)b * 16, smem);
 }
 
-// Split of the K loop: T = K / KSTEP steps = S waves x niter iterations x NSTEP.
-struct GemvSplit { int nstep, S, niter; };
+// Split of the K loop: T = K / KSTEP steps = nchunk chunks of NSTEP steps over
+// S <= 8 waves (the largest NSTEP dividing T; as many waves as there are
+// chunks, up to 8, shares differing by at most one chunk).
+struct GemvSplit { int nstep, S, nchunk; };
 inline GemvSplit gemv_split(int64_t T, int maxstep) {
-  for (int ns = maxstep; ns >= 1; ns >>= 1) {
-    if (T % ns) continue;
-    const int64_t steps = T / ns;
-    for (int S = 8; S >= 1; S--)
-      if (steps % S == 0) return GemvSplit{ns, S, (int)(steps / S)};
-  }
-  return GemvSplit{1, 1, (int)T};
+  int ns = maxstep;
+  while (ns > 1 && T % ns) ns >>= 1;
+  const int64_t chunks = T / ns;
+  return GemvSplit{ns, (int)(chunks < 8 ? chunks : 8), (int)chunks};
 }
 
 template <int WDT, int TN, int NSTEP, bool XLDS>
@@ -867,7 +870,7 @@ void gemv_go(const GemvSplit& sp, const uint16_t* x, int64_t M, int64_t N, int64
   constexpr int KCH = NSTEP * (WTraits<WDT>::bits == 4 ? 128 : 64);
   const size_t lds = (XLDS ? (size_t)sp.S * (4 * KCH * 2 + 64) : 0) + (size_t)sp.S * TN * 1024;
   const int gshift = group == 32 ? 5 : group == 64 ? 6 : 7;
-  k_gemv<WDT, TN, NSTEP, XLDS><<<grid, 64 * sp.S, lds, s>>>(x, (int)M, N, K, w, sc, gshift, ch, alpha, y, sp.niter);
+  k_gemv<WDT, TN, NSTEP, XLDS><<<grid, 64 * sp.S, lds, s>>>(x, (int)M, N, K, w, sc, gshift, ch, alpha, y, sp.nchunk);
 }
 
 template <int WDT, int TN, bool XLDS>
