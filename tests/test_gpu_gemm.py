@@ -234,12 +234,27 @@ def test_gemv_uneven_k_split(W, kind, M, N, K):
 @pytest.mark.parametrize("kind", ["int4", "mxfp4", "e4m3"])
 @pytest.mark.parametrize("M", [5, 8, 13, 16])
 @pytest.mark.parametrize("N,K", [(300, 2048), (1000, 4096), (64, 4096)])
-def test_gemv_x_once_per_workgroup(W, kind, M, N, K):
-    # 5 <= M <= 16 with K = 2048 or 4096 takes the form that stages x in LDS
-    # once per workgroup of 64 columns: ragged last workgroup (300 = 4 x 64 +
-    # 44, 1000 = 15 x 64 + 40), a single workgroup, every M that leaves MFMA
-    # rows without a token
+def test_gemv_few_tiles_5_to_16(W, kind, M, N, K):
+    # 5 <= M <= 16 with at most one 16-column tile per CU: one tile and up to
+    # 16 waves per workgroup (ragged last tile, a single workgroup, every M
+    # that leaves MFMA rows without a token)
     g = np.random.default_rng(900 + M * 3 + N + K)
+    Wf = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
+    Wf[:, g.choice(K, 5, replace=False)] *= 30
+    xbits = to_bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    args, wdeq, chan = _prep(W, kind, Wf)
+    banner("gemv few tiles", kind, M, N, K)
+    _check(W.wq_gemm(dev_bf16(xbits), *args, N), xbits, wdeq, chan)
+
+
+@pytest.mark.parametrize("kind", ["int4", "mxfp4", "e4m3"])
+@pytest.mark.parametrize("M", [5, 16])
+@pytest.mark.parametrize("N,K", [(4200, 2048), (4136, 4096)])
+def test_gemv_x_once_per_workgroup(W, kind, M, N, K):
+    # 5 <= M <= 16, more 16-column tiles than CUs, K = 2048 or 4096: 64 columns
+    # per 16-wave workgroup with x staged once in LDS (ragged last workgroups
+    # of 40 and 40 columns)
+    g = np.random.default_rng(950 + M * 3 + N + K)
     Wf = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
     Wf[:, g.choice(K, 5, replace=False)] *= 30
     xbits = to_bf16_bits(g.standard_normal((M, K)).astype(np.float32))

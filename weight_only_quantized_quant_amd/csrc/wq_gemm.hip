@@ -138,7 +138,7 @@ __device__ __forceinline__ scale_t<WDT> scale_of(__amdgpu_buffer_rsrc_t r, uint3
 // chunks [w nchunk / S, (w + 1) nchunk / S), so the waves' shares differ by at
 // most one chunk whatever K is.
 template <int WDT, int TN, int NSTEP, bool XLDS>
-__global__ __launch_bounds__(512) void k_gemv(const uint16_t* __restrict__ x, int M, int64_t N, int64_t K,
+__global__ __launch_bounds__(1024) void k_gemv(const uint16_t* __restrict__ x, int M, int64_t N, int64_t K,
                                              const uint8_t* __restrict__ w, const void* __restrict__ sc,
                                              int group_shift, const float* __restrict__ chscale, float alpha,
                                              uint16_t* __restrict__ y, int nchunk) {
@@ -853,35 +853,38 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_ring(const uint16_t* __restric
 }
 
 // Split of the K loop: T = K / KSTEP steps = nchunk chunks of NSTEP steps over
-// S <= 8 waves (the largest NSTEP dividing T; as many waves as there are
-// chunks, up to 8, shares differing by at most one chunk).
+// S <= smax waves (the largest NSTEP dividing T; as many waves as there are
+// chunks, up to smax, shares differing by at most one chunk).
 struct GemvSplit { int nstep, S, nchunk; };
-inline GemvSplit gemv_split(int64_t T, int maxstep) {
+inline GemvSplit gemv_split(int64_t T, int maxstep, int smax) {
   int ns = maxstep;
   while (ns > 1 && T % ns) ns >>= 1;
   const int64_t chunks = T / ns;
-  return GemvSplit{ns, (int)(chunks < 8 ? chunks : 8), (int)chunks};
+  return GemvSplit{ns, (int)(chunks < smax ? chunks : smax), (int)chunks};
 }
 
 template <int WDT, int TN, int NSTEP, bool XLDS>
-void gemv_go(const GemvSplit& sp, const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w,
+hipError_t gemv_go(const GemvSplit& sp, const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w,
              const void* sc, int group, const float* ch, float alpha, uint16_t* y, hipStream_t s) {
   const unsigned grid = (unsigned)((N + 16 * TN - 1) / (16 * TN));
   constexpr int KCH = NSTEP * (WTraits<WDT>::bits == 4 ? 128 : 64);
   const size_t lds = (XLDS ? (size_t)sp.S * (4 * KCH * 2 + 64) : 0) + (size_t)sp.S * TN * 1024;
   const int gshift = group == 32 ? 5 : group == 64 ? 6 : 7;
+  const hipError_t e = allow_lds<k_gemv<WDT, TN, NSTEP, XLDS>>(lds);
+  if (e != hipSuccess) return e;
   k_gemv<WDT, TN, NSTEP, XLDS><<<grid, 64 * sp.S, lds, s>>>(x, (int)M, N, K, w, sc, gshift, ch, alpha, y, sp.nchunk);
+  return hipSuccess;
 }
 
 template <int WDT, int TN, bool XLDS>
-void gemv_nstep(const GemvSplit& sp, const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w,
-                const void* sc, int group, const float* ch, float alpha, uint16_t* y, hipStream_t s) {
+hipError_t gemv_nstep(const GemvSplit& sp, const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w,
+                      const void* sc, int group, const float* ch, float alpha, uint16_t* y, hipStream_t s) {
   switch (sp.nstep) {
-    case 8: if constexpr (WTraits<WDT>::bits == 8) { gemv_go<WDT, TN, 8, XLDS>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s); break; }
+    case 8: if constexpr (WTraits<WDT>::bits == 8) return gemv_go<WDT, TN, 8, XLDS>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s);
             [[fallthrough]];
-    case 4: gemv_go<WDT, TN, 4, XLDS>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s); break;
-    case 2: gemv_go<WDT, TN, 2, XLDS>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s); break;
-    default: gemv_go<WDT, TN, 1, XLDS>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s); break;
+    case 4: return gemv_go<WDT, TN, 4, XLDS>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s);
+    case 2: return gemv_go<WDT, TN, 2, XLDS>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s);
+    default: return gemv_go<WDT, TN, 1, XLDS>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s);
   }
 }
 
@@ -1224,6 +1227,9 @@ bool ring_path(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t
   if (K % (KSTEP * RING_NW) || 16 * K * 2 > 0x7FFFFFF0LL) return false;
   const int64_t spw = K / (KSTEP * RING_NW);
   if (M <= 4) {
+    // (8 or 16 waves per tile when the tiles are few, each with a shorter K
+    // slice, measured no faster: N = 4096, K = 4096: 5.4 against 5.2-5.4 us;
+    // N = 8192: 7.6 against 6.6 us)
     switch (spw) {
       case 1: st = ring_go<WDT, 1, GSH>(M, x, N, K, w, sc, ch, alpha, y, s); return true;
       case 2: st = ring_go<WDT, 2, GSH>(M, x, N, K, w, sc, ch, alpha, y, s); return true;
@@ -1233,6 +1239,15 @@ bool ring_path(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t
       default: return false;
     }
   }
+  // when the 16-column tiles alone do not fill the CUs, the general form
+  // (one tile and up to 16 waves per workgroup) is faster for 4 < M <= 16
+  // (measured N = 1024-4096: 7.9-8.9 us against 11.3-12.1 us)
+  int ncu = 0;
+  if (cu_count(&ncu) != hipSuccess) {
+    st = WQ_EHIP;
+    return true;
+  }
+  if ((N + 15) / 16 <= ncu) return false;
   constexpr int SW = WTraits<WDT>::bits == 4 ? 1 : 2;          // steps per wave at K = 2048
   if (K == 2048) { st = wide_go<WDT, SW, GSH>(M, x, N, K, w, sc, ch, alpha, y, s); return true; }
   if (K == 4096) { st = wide_go<WDT, 2 * SW, GSH>(M, x, N, K, w, sc, ch, alpha, y, s); return true; }
@@ -1267,12 +1282,19 @@ wq_status launch_gemv(const uint16_t* x, int64_t M, int64_t N, int64_t K, const 
     // K = 128*j with j odd only matters for 8-bit weights, whose step is 64: always divisible
     return WQ_EINVAL;
   }
-  const GemvSplit sp = gemv_split(K / KSTEP, MAXSTEP);
-  const bool xlds = M <= 4;
-  if (xlds) gemv_nstep<WDT, 1, true>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s);
-  else if (M <= 4) gemv_nstep<WDT, 1, false>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s);
-  else gemv_nstep<WDT, 2, false>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s);
-  return wq_launch_status();
+  // up to 16 waves per workgroup when the column tiles alone do not fill the
+  // CUs; two 16-column tiles per workgroup for M > 4 only when there are
+  // enough of them
+  int ncu = 0;
+  if (cu_count(&ncu) != hipSuccess) return WQ_EHIP;
+  const int64_t tiles = (N + 15) / 16;
+  const bool two = M > 4 && tiles >= 4 * (int64_t)ncu;
+  const GemvSplit sp = gemv_split(K / KSTEP, MAXSTEP, (two ? tiles / 2 : tiles) <= ncu ? 16 : 8);
+  hipError_t e;
+  if (M <= 4) e = gemv_nstep<WDT, 1, true>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s);
+  else if (!two) e = gemv_nstep<WDT, 1, false>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s);
+  else e = gemv_nstep<WDT, 2, false>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s);
+  return e != hipSuccess ? WQ_EHIP : wq_launch_status();
 }
 
 template <int WDT>
