@@ -216,6 +216,22 @@ def test_gemv_int4_offset_activations(W, M):
 
 
 @pytest.mark.parametrize("kind", ["int4", "mxfp4", "e4m3"])
+@pytest.mark.parametrize("M", [1, 3, 4])
+def test_gemv_ring_28_steps(W, kind, M):
+    # 28 ring steps per wave: K = 14336 for 4-bit weights (the MLP down
+    # projection's K), 7168 for E4M3; 300 columns (ragged last tile)
+    K = 7168 if kind == "e4m3" else 14336
+    N = 300
+    g = np.random.default_rng(1300 + M + K)
+    Wf = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
+    Wf[:, g.choice(K, 6, replace=False)] *= 30
+    xbits = to_bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    args, wdeq, chan = _prep(W, kind, Wf)
+    banner("gemv ring 28 steps", kind, M, N, K)
+    _check(W.wq_gemm(dev_bf16(xbits), *args, N), xbits, wdeq, chan)
+
+
+@pytest.mark.parametrize("kind", ["int4", "mxfp4", "e4m3"])
 @pytest.mark.parametrize("M", [1, 4, 16])
 @pytest.mark.parametrize("N,K", [(100, 11008), (70, 14336), (90, 640)])
 def test_gemv_uneven_k_split(W, kind, M, N, K):

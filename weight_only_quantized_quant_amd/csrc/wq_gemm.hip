@@ -624,7 +624,7 @@ __host__ __device__ constexpr int ring_wave_bytes(int spwe, int r, bool half, bo
   const int ksl = spwe * kstep;
   const int xr = half ? 2 : 1;
   const int sbrow = (ksl >> gshift_of<WDT>(GSH)) * scale_bytes<WDT>();
-  const int sbytes = WDT == W_FP8 ? 0 : 16 * (sbrow < 16 ? 16 : sbrow);
+  const int sbytes = WDT == W_FP8 ? 0 : 16 * (sbrow < 16 ? 16 : (sbrow + 15) / 16 * 16);
   const int ns = ring_slots(spwe, r);
   const int ring = xs ? ns * (1024 + xr * 4 * kstep * 2) : (ring_regw<WDT>(xs) ? 0 : ns * 1024) + xr * m * ksl * 2;
   return ring + ((sbytes + 15) & ~15);
@@ -697,7 +697,7 @@ __device__ __forceinline__ void gemv_ring_tile(const uint16_t* __restrict__ x, i
   // scales of the slice (16 MFMA columns, row stride srs).  With XS a slot
   // holds the step's 1 KB of weights, then 4 token rows of x per K half.
   constexpr int XR = HALF ? 2 : 1;
-  constexpr uint32_t srs = sbrow < 16 ? 16 : sbrow;
+  constexpr uint32_t srs = sbrow < 16 ? 16 : (sbrow + 15) / 16 * 16;   // LDS row stride of the scales
   constexpr int XRB = KSTEP * 2;                              // bytes of one x row of a step
   constexpr int XCH = 4 * XRB;                                // x chunk of one K half
   constexpr int SLOT = XS ? 1024 + XR * XCH : 1024;
@@ -708,10 +708,12 @@ __device__ __forceinline__ void gemv_ring_tile(const uint16_t* __restrict__ x, i
   uint8_t* xl = ring + (REGW ? 0 : NS * SLOT);
   uint8_t* sl = xl + (XS ? 0 : XR * M * XROW);
 
-  // 1) scales of the slice.  When a row of the slice holds >= 16 bytes of
-  //    scales (a multiple of 16), they arrive by DMA, 16 bytes per lane; for
-  //    thinner slices every lane loads its own per-step scales instead (a 16-byte
-  //    window could leave the buffer range at the last row and read as zeros).
+  // 1) scales of the slice.  When a row of the slice holds at least 16 bytes
+  //    of scales, they arrive by DMA, 16 bytes per lane, the row's window
+  //    rounded up to whole 16-byte pieces (the bytes past the slice are not
+  //    used; past the buffer range they read as zeros); for thinner slices
+  //    every lane loads its own per-step scales instead (a 16-byte window
+  //    could leave the buffer range at the last row and read as zeros).
   constexpr bool sdma = sbrow >= 16;
   uint32_t svr[SPWE];
   if constexpr (WDT != W_FP8) {
@@ -1236,6 +1238,7 @@ bool ring_path(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t
       case 4: st = ring_go<WDT, 4, GSH>(M, x, N, K, w, sc, ch, alpha, y, s); return true;
       case 8: st = ring_go<WDT, 8, GSH>(M, x, N, K, w, sc, ch, alpha, y, s); return true;
       case 16: st = ring_go<WDT, 16, GSH>(M, x, N, K, w, sc, ch, alpha, y, s); return true;
+      case 28: st = ring_go<WDT, 28, GSH>(M, x, N, K, w, sc, ch, alpha, y, s); return true;   // K = 14336, 4-bit
       default: return false;
     }
   }
