@@ -150,6 +150,21 @@ def test_decode_repeatable_with_cached_weights(W, decode_weights, M):
 
 
 @pytest.mark.parametrize("kind", ["int4", "mxfp4", "e4m3"])
+@pytest.mark.parametrize("M", [20, 33, 64, 65])
+def test_gemm_row_groups(W, kind, M):
+    # 16 < M <= 64 runs the decode forms once per group of 16 rows (a last
+    # group of 4, 1 and 16 rows); M = 65 takes the prefill GEMM
+    N, K = 1000, 2048
+    g = np.random.default_rng(1500 + M)
+    Wf = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
+    Wf[:, g.choice(K, 5, replace=False)] *= 30
+    xbits = to_bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    args, wdeq, chan = _prep(W, kind, Wf)
+    banner("gemm row groups", kind, M, N, K)
+    _check(W.wq_gemm(dev_bf16(xbits), *args, N), xbits, wdeq, chan)
+
+
+@pytest.mark.parametrize("kind", ["int4", "mxfp4", "e4m3"])
 @pytest.mark.parametrize("M,N,K", [(300, 520, 512), (17, 256, 256), (512, 512, 1024), (257, 33, 128)])
 def test_gemm_ragged(W, kind, M, N, K):
     g = np.random.default_rng(M + N + K)

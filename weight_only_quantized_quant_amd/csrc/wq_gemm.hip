@@ -1142,6 +1142,8 @@ __global__ __launch_bounds__(64 * WW) __attribute__((amdgpu_waves_per_eu(WW / 4,
 // ring beat deeper rings (requests all in flight arrive in an order that
 // bunches the dequantization work at the end) and 8-wave splits.
 constexpr int RING_NW = 4;
+// row groups of 16 that wq_gemm sends through the decode forms (16 < M <= 64)
+constexpr int WQ_DECODE_GROUPS = 4;
 constexpr int RING_DEPTH = 2;
 // 4 < M <= 16: two 16-column tiles per workgroup share every x chunk, which
 // halves the x traffic from L2 (each workgroup reads the whole x slice).
@@ -1342,14 +1344,26 @@ wq_status wq_gemm(const void* x_bf16, int64_t M, int64_t N, int64_t K, const voi
   const uint8_t* w = (const uint8_t*)wqp;
   uint16_t* y = (uint16_t*)y_bf16;
   const float* ch = wdt == W_FP8 ? (const float*)w_scales : nullptr;
-  if (M <= 16) {
-    switch (wdt) {
-      case W_INT4: return launch_gemv<W_INT4>(x, M, N, K, w, w_scales, group, ch, alpha, y, s);
-      case W_FP4: return launch_gemv<W_FP4>(x, M, N, K, w, w_scales, group, ch, alpha, y, s);
-      case W_NV4: return launch_gemv<W_NV4>(x, M, N, K, w, w_scales, group, ch, alpha, y, s);
-      case W_UINT4: return launch_gemv<W_UINT4>(x, M, N, K, w, w_scales, group, ch, alpha, y, s);
-      default: return launch_gemv<W_FP8>(x, M, N, K, w, w_scales, group, ch, alpha, y, s);
+  // M <= 16: the decode forms.  16 < M <= 64: the GEMM's 256-row tiles leave
+  // most CUs idle (N / 256 workgroups: 90 us at N = 14336, K = 4096 for any
+  // M up to 512), so the rows go through the decode forms in groups of 16,
+  // each launch streaming the weights once (about 13 us per group there).
+  if (M <= WQ_DECODE_GROUPS * 16) {
+    for (int64_t m0 = 0; m0 < M; m0 += 16) {
+      const int64_t mg = M - m0 < 16 ? M - m0 : 16;
+      const uint16_t* xg = x + m0 * K;
+      uint16_t* yg = y + m0 * N;
+      wq_status st;
+      switch (wdt) {
+        case W_INT4: st = launch_gemv<W_INT4>(xg, mg, N, K, w, w_scales, group, ch, alpha, yg, s); break;
+        case W_FP4: st = launch_gemv<W_FP4>(xg, mg, N, K, w, w_scales, group, ch, alpha, yg, s); break;
+        case W_NV4: st = launch_gemv<W_NV4>(xg, mg, N, K, w, w_scales, group, ch, alpha, yg, s); break;
+        case W_UINT4: st = launch_gemv<W_UINT4>(xg, mg, N, K, w, w_scales, group, ch, alpha, yg, s); break;
+        default: st = launch_gemv<W_FP8>(xg, mg, N, K, w, w_scales, group, ch, alpha, yg, s); break;
+      }
+      if (st != WQ_OK) return st;
     }
+    return WQ_OK;
   }
   switch (wdt) {
     case W_INT4: return launch_gemm<W_INT4>(x, M, N, K, w, w_scales, group, ch, alpha, y, s);
