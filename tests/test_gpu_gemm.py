@@ -279,6 +279,24 @@ def test_gemv_few_tiles_5_to_16(W, kind, M, N, K):
 
 
 @pytest.mark.parametrize("kind", ["int4", "mxfp4", "e4m3"])
+@pytest.mark.parametrize("M", [5, 11, 16])
+@pytest.mark.parametrize("N,K", [(300, 14336), (70, 1152), (4500, 1536), (40, 640)])
+def test_gemv_x_through_lds(W, kind, M, N, K):
+    # 5 <= M <= 16, one 16-column tile per workgroup, x rows fetched whole and
+    # staged in LDS chunk by chunk with the next chunk in flight: 7 chunks per
+    # wave at K = 14336 (odd count), one chunk per wave at K = 1152 and 640
+    # (9 and 5 waves), 8 waves per workgroup when the tiles outnumber the CUs
+    # (N = 4500)
+    g = np.random.default_rng(970 + M * 3 + N + K)
+    Wf = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
+    Wf[:, g.choice(K, 5, replace=False)] *= 30
+    xbits = to_bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    args, wdeq, chan = _prep(W, kind, Wf)
+    banner("gemv x through lds", kind, M, N, K)
+    _check(W.wq_gemm(dev_bf16(xbits), *args, N), xbits, wdeq, chan)
+
+
+@pytest.mark.parametrize("kind", ["int4", "mxfp4", "e4m3"])
 @pytest.mark.parametrize("M", [5, 16])
 @pytest.mark.parametrize("N,K", [(4200, 2048), (4136, 4096)])
 def test_gemv_x_once_per_workgroup(W, kind, M, N, K):

@@ -124,7 +124,8 @@ def _check(y_dev, xbits, wdeq, g, rows=None):
 
 @pytest.mark.parametrize("M,N,K", [(1, 1000, 384), (3, 520, 512), (4, 272, 8192), (1, 300, 8192), (8, 272, 1024),
                                    (16, 300, 4096), (5, 17, 128), (2, 4096, 2048), (17, 256, 256), (300, 520, 512),
-                                   (257, 33, 128), (512, 512, 1024)])
+                                   (257, 33, 128), (512, 512, 1024),
+                                   (9, 300, 14336), (12, 4500, 1536)])
 def test_gemm_ragged(W, M, N, K):
     r = np.random.default_rng(M * 7 + N + K)
     Wf = (r.standard_normal((N, K)) * 0.02).astype(np.float32)

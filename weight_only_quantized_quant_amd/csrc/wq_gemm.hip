@@ -132,7 +132,9 @@ __device__ __forceinline__ scale_t<WDT> scale_of(__amdgpu_buffer_rsrc_t r, uint3
 // LDS region (M x NSTEP*KSTEP bf16, one 16-byte load per lane per row) next to
 // a 64-byte zero block; lanes whose MFMA row is >= M read the zero block.
 // No workgroup barrier is needed: LDS operations of one wave execute in order.
-// Otherwise x is read with buffer loads (rows >= M read as zeros).
+// Otherwise x is read with buffer loads (rows >= M read as zeros); for
+// 4 < M <= 16 that is left to two tiles per workgroup, one tile stages x in
+// LDS (k_gemv_x16).
 // Issue order per chunk: x staging loads, scales, weights.
 // K splits into nchunk chunks of NSTEP steps; wave w of the S waves takes
 // chunks [w nchunk / S, (w + 1) nchunk / S), so the waves' shares differ by at
@@ -251,6 +253,129 @@ __global__ __launch_bounds__(1024) void k_gemv(const uint16_t* __restrict__ x, i
     if (m >= M || col >= N) continue;
     float s = 0.0f;
     for (int wv = 0; wv < S; wv++) s += red[((wv * TN + t) * 16 + m) * 16 + n];
+    s *= WDT == W_FP8 ? chscale[col] * alpha : alpha;
+    y[(int64_t)m * N + col] = (uint16_t)f32_to_bf16_bits(s);
+  }
+}
+
+// 4 < M <= 16, one 16-column tile per workgroup: each chunk's x rows are
+// fetched whole (consecutive lanes read consecutive 16-byte pieces of a row)
+// and pass through the wave's LDS region, piece p of row r at p ^ (r & 15), so
+// that the 16 rows of one fragment read sit in distinct banks.  Read straight
+// into the MFMA layout instead, a lane's four pieces of a row lie 64 bytes
+// apart and each load touches two cache lines per row for one quarter of
+// their bytes.  The next chunk's x, scales and weights are in flight while the
+// current one is multiplied (two register sets, used in turn; a set past the
+// wave's last chunk, and an x row past M, load from an offset outside the
+// buffer range, which returns zeros without a memory access, so every load is
+// issued unconditionally and the wait counts stay fixed).
+template <int WDT, int NSTEP>
+__global__ __launch_bounds__(1024) void k_gemv_x16(const uint16_t* __restrict__ x, int M, int64_t N, int64_t K,
+                                                  const uint8_t* __restrict__ w, const void* __restrict__ sc,
+                                                  int group_shift, const float* __restrict__ chscale, float alpha,
+                                                  uint16_t* __restrict__ y, int nchunk) {
+  constexpr int EPL = WTraits<WDT>::bits == 4 ? 32 : 16;   // elements per lane per step
+  constexpr int KSTEP = 4 * EPL;                            // K covered by a wave per step
+  constexpr int KCH = NSTEP * KSTEP;                        // K per wave per chunk
+  constexpr int MF = EPL / 8;                               // MFMAs per step
+  constexpr int BPE2 = WTraits<WDT>::bits == 4 ? 1 : 2;     // bytes per 2 elements
+  constexpr int SB = scale_bytes<WDT>();
+  constexpr int XCH = KCH / 8;                              // 16-byte pieces per x row of a chunk
+  constexpr int XL = 16 * XCH / 64;                         // x loads per lane per chunk
+  constexpr int XRB = KCH * 2;                              // bytes per x row of a chunk
+  static_assert(XCH % 16 == 0 && XCH <= 64, "x pieces are swizzled in groups of 16");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+  const int S = blockDim.x >> 6;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nl = lane & 15, g = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const uint32_t rowbytes = (uint32_t)(K * BPE2 / 2);
+  const int64_t nrows = N - n0 < 16 ? N - n0 : 16;
+  const int gs = gshift_of<WDT>(group_shift);
+  const uint32_t spr = (uint32_t)(K >> gs);
+  const auto rw = make_rsrc(w + n0 * rowbytes, nrows * rowbytes);
+  const auto rs = make_rsrc(reinterpret_cast<const uint8_t*>(sc) + (WDT == W_FP8 ? 0 : n0 * spr * SB),
+                            WDT == W_FP8 ? 0 : nrows * spr * SB);
+  const auto rx = make_rsrc(x, (int64_t)M * K * 2);
+  const int c0 = (int)((int64_t)wave * nchunk / S), niter = (int)((int64_t)(wave + 1) * nchunk / S) - c0;
+  constexpr uint32_t OUT = 0x7FFFFFF0u;                     // past every range (all <= this many bytes)
+  constexpr uint32_t SOUT = OUT / 4;                        // scale index past every scale range
+  uint8_t* xw = smem + wave * 16 * XRB;
+  float* red = reinterpret_cast<float*>(smem + S * 16 * XRB);
+  const int xtr = nl < M ? nl : 0;                          // rows past M read row 0; dropped
+
+  struct Chunk {
+    u32x4_t xs[XL];
+    u32x4_t wr[NSTEP];
+    uint32_t sv[NSTEP];                                     // raw bits, converted at the use
+  };
+  auto issue = [&](Chunk& b, int it) {
+    const bool ok = it < niter;
+    const uint32_t k0 = (uint32_t)((c0 + it) * KCH);
+#pragma unroll
+    for (int i = 0; i < XL; i++) {
+      const int f = 64 * i + lane, r = f / XCH, p = f % XCH;
+      b.xs[i] = bld16(rx, ok && r < M ? (uint32_t)(r * (uint32_t)K + k0 + 8 * p) * 2 : OUT);
+    }
+#pragma unroll
+    for (int c = 0; c < NSTEP; c++) {
+      const uint32_t kk = k0 + c * KSTEP + EPL * g;
+      b.sv[c] = scale_raw_of<WDT>(rs, ok ? (uint32_t)nl * spr + (kk >> gs) : SOUT);
+    }
+#pragma unroll
+    for (int c = 0; c < NSTEP; c++) {
+      const uint32_t kk = k0 + c * KSTEP + EPL * g;
+      b.wr[c] = bld16(rw, ok ? (uint32_t)nl * rowbytes + kk * BPE2 / 2 : OUT);
+    }
+  };
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto consume = [&](Chunk& b) {
+    // the previous chunk's fragment reads of the region come first
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int i = 0; i < XL; i++) {
+      const int f = 64 * i + lane, r = f / XCH, p = f % XCH;
+      if (r < M) *reinterpret_cast<u32x4_t*>(xw + r * XRB + ((p ^ (r & 15)) << 4)) = b.xs[i];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int c = 0; c < NSTEP; c++) {
+      bf16x8_t xa[MF];
+#pragma unroll
+      for (int j = 0; j < MF; j++) {
+        const int p = (c * KSTEP + EPL * g + 8 * j) >> 3;
+        xa[j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(xw + xtr * XRB + ((p ^ (xtr & 15)) << 4)));
+      }
+      bf16x8_t bq[4];
+      dequant16<WDT>(b.wr[c], scale_from_raw<WDT>(b.sv[c]), bq);
+#pragma unroll
+      for (int j = 0; j < MF; j++) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[j], bq[j], acc, 0, 0, 0);
+    }
+  };
+  Chunk ca, cb;
+  issue(ca, 0);
+  for (int it = 0; it < niter; it += 2) {
+    issue(cb, it + 1);
+    consume(ca);
+    issue(ca, it + 2);
+    if (it + 1 < niter) consume(cb);
+  }
+
+  // acc[i] holds C[m = 4g + i][n = nl]
+#pragma unroll
+  for (int i = 0; i < 4; i++) red[(wave * 16 + 4 * g + i) * 16 + nl] = acc[i];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < 256; idx += blockDim.x) {
+    const int m = idx >> 4, n = idx & 15;
+    const int64_t col = n0 + n;
+    if (m >= M || col >= N) continue;
+    float s = 0.0f;
+    for (int wv = 0; wv < S; wv++) s += red[(wv * 16 + m) * 16 + n];
     s *= WDT == W_FP8 ? chscale[col] * alpha : alpha;
     y[(int64_t)m * N + col] = (uint16_t)f32_to_bf16_bits(s);
   }
@@ -878,6 +1003,19 @@ hipError_t gemv_go(const GemvSplit& sp, const uint16_t* x, int64_t M, int64_t N,
   return hipSuccess;
 }
 
+template <int WDT, int NSTEP>
+hipError_t x16_go(const GemvSplit& sp, const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w,
+                  const void* sc, int group, const float* ch, float alpha, uint16_t* y, hipStream_t s) {
+  const unsigned grid = (unsigned)((N + 15) / 16);
+  constexpr int KCH = NSTEP * (WTraits<WDT>::bits == 4 ? 128 : 64);
+  const size_t lds = (size_t)sp.S * (16 * KCH * 2 + 1024);
+  const int gshift = group == 32 ? 5 : group == 64 ? 6 : 7;
+  const hipError_t e = allow_lds<k_gemv_x16<WDT, NSTEP>>(lds);
+  if (e != hipSuccess) return e;
+  k_gemv_x16<WDT, NSTEP><<<grid, 64 * sp.S, lds, s>>>(x, (int)M, N, K, w, sc, gshift, ch, alpha, y, sp.nchunk);
+  return hipSuccess;
+}
+
 template <int WDT, int TN, bool XLDS>
 hipError_t gemv_nstep(const GemvSplit& sp, const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w,
                       const void* sc, int group, const float* ch, float alpha, uint16_t* y, hipStream_t s) {
@@ -1297,7 +1435,16 @@ wq_status launch_gemv(const uint16_t* x, int64_t M, int64_t N, int64_t K, const 
   const GemvSplit sp = gemv_split(K / KSTEP, MAXSTEP, (two ? tiles / 2 : tiles) <= ncu ? 16 : 8);
   hipError_t e;
   if (M <= 4) e = gemv_nstep<WDT, 1, true>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s);
-  else if (!two) e = gemv_nstep<WDT, 1, false>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s);
+  else if (!two) {
+    // x through LDS; a chunk row's 16-byte x pieces come in groups of 16
+    // (one step for 4-bit weights, two for 8-bit, whose step count is even
+    // since K % 128 == 0; one step measured faster than two for 4-bit,
+    // N = 1792-8192, K = 4096-14336, M = 5-16)
+    constexpr int XS = WTraits<WDT>::bits == 4 ? 1 : 2;
+    const GemvSplit sx = gemv_split(K / KSTEP, XS, tiles <= ncu ? 16 : 8);
+    e = sx.nstep == XS ? x16_go<WDT, XS>(sx, x, M, N, K, w, sc, group, ch, alpha, y, s)
+                       : gemv_nstep<WDT, 1, false>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s);
+  }
   else e = gemv_nstep<WDT, 2, false>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s);
   return e != hipSuccess ? WQ_EHIP : wq_launch_status();
 }
