@@ -280,13 +280,14 @@ def test_gemv_few_tiles_5_to_16(W, kind, M, N, K):
 
 @pytest.mark.parametrize("kind", ["int4", "mxfp4", "e4m3"])
 @pytest.mark.parametrize("M", [5, 11, 16])
-@pytest.mark.parametrize("N,K", [(300, 14336), (70, 1152), (4500, 1536), (40, 640)])
+@pytest.mark.parametrize("N,K", [(300, 14336), (70, 1152), (4500, 1536), (40, 640), (4100, 8192)])
 def test_gemv_x_through_lds(W, kind, M, N, K):
-    # 5 <= M <= 16, one 16-column tile per workgroup, x rows fetched whole and
-    # staged in LDS chunk by chunk with the next chunk in flight: 7 chunks per
-    # wave at K = 14336 (odd count), one chunk per wave at K = 1152 and 640
-    # (9 and 5 waves), 8 waves per workgroup when the tiles outnumber the CUs
-    # (N = 4500)
+    # 5 <= M <= 16 with x rows fetched whole and staged in LDS chunk by chunk,
+    # the next chunk in flight: 7 chunks per wave at K = 14336 (odd count), one
+    # chunk per wave at K = 1152 and 640 (9 and 5 waves); two 16-column tiles
+    # per workgroup when the tiles outnumber the CUs, with a last workgroup of
+    # 16 + 4 columns (N = 4500) or of 4 columns and an empty second tile
+    # (N = 4100)
     g = np.random.default_rng(970 + M * 3 + N + K)
     Wf = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
     Wf[:, g.choice(K, 5, replace=False)] *= 30

@@ -128,18 +128,17 @@ __device__ __forceinline__ scale_t<WDT> scale_of(__amdgpu_buffer_rsrc_t r, uint3
   return scale_from_raw<WDT>(scale_raw_of<WDT>(r, idx));
 }
 
-// XLDS (M <= 4): each wave stages the x rows of its own K chunk in a private
-// LDS region (M x NSTEP*KSTEP bf16, one 16-byte load per lane per row) next to
-// a 64-byte zero block; lanes whose MFMA row is >= M read the zero block.
-// No workgroup barrier is needed: LDS operations of one wave execute in order.
-// Otherwise x is read with buffer loads (rows >= M read as zeros); for
-// 4 < M <= 16 that is left to two tiles per workgroup, one tile stages x in
-// LDS (k_gemv_x16).
+// General decode form for M <= 4 (K not taken by the ring): one 16-column
+// tile per workgroup.  Each wave stages the x rows of its own K chunk in a
+// private LDS region (M x NSTEP*KSTEP bf16, one 16-byte load per lane per row)
+// next to a 64-byte zero block; lanes whose MFMA row is >= M read the zero
+// block.  No workgroup barrier is needed: LDS operations of one wave execute
+// in order.
 // Issue order per chunk: x staging loads, scales, weights.
 // K splits into nchunk chunks of NSTEP steps; wave w of the S waves takes
 // chunks [w nchunk / S, (w + 1) nchunk / S), so the waves' shares differ by at
 // most one chunk whatever K is.
-template <int WDT, int TN, int NSTEP, bool XLDS>
+template <int WDT, int NSTEP>
 __global__ __launch_bounds__(1024) void k_gemv(const uint16_t* __restrict__ x, int M, int64_t N, int64_t K,
                                              const uint8_t* __restrict__ w, const void* __restrict__ sc,
                                              int group_shift, const float* __restrict__ chscale, float alpha,
@@ -151,15 +150,15 @@ __global__ __launch_bounds__(1024) void k_gemv(const uint16_t* __restrict__ x, i
   constexpr int BPE2 = WTraits<WDT>::bits == 4 ? 1 : 2;     // bytes per 2 elements
   constexpr int SB = scale_bytes<WDT>();
   constexpr int XW = 4 * KCH * 2 + 64;                      // per-wave x region (up to 4 rows)
-  static_assert(KCH == 512 || !XLDS || KCH < 512, "x staging uses one 16-byte chunk per lane per 512 k");
+  static_assert(KCH <= 512, "x staging uses one 16-byte chunk per lane per 512 k");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int S = blockDim.x >> 6;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nl = lane & 15, g = lane >> 4;
-  const int64_t n0 = (int64_t)blockIdx.x * 16 * TN;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
   const uint32_t rowbytes = (uint32_t)(K * BPE2 / 2);
-  const int64_t nrows = N - n0 < 16 * TN ? N - n0 : 16 * TN;
+  const int64_t nrows = N - n0 < 16 ? N - n0 : 16;
   const int gs = gshift_of<WDT>(group_shift);               // log2 of the scale group
   const uint32_t spr = (uint32_t)(K >> gs);                  // scales per row
   const auto rw = make_rsrc(w + n0 * rowbytes, nrows * rowbytes);
@@ -170,96 +169,73 @@ __global__ __launch_bounds__(1024) void k_gemv(const uint16_t* __restrict__ x, i
   const uint32_t kbase = (uint32_t)(c0 * KCH);
 
   uint8_t* xw = smem + wave * XW;                            // this wave's x rows, then zeros
-  float* red = reinterpret_cast<float*>(smem + (XLDS ? S * XW : 0));
-  if constexpr (XLDS) {
-    if (lane < 4) *reinterpret_cast<u32x4_t*>(xw + 4 * KCH * 2 + 16 * lane) = u32x4_t{0u, 0u, 0u, 0u};
-  }
+  float* red = reinterpret_cast<float*>(smem + S * XW);
+  if (lane < 4) *reinterpret_cast<u32x4_t*>(xw + 4 * KCH * 2 + 16 * lane) = u32x4_t{0u, 0u, 0u, 0u};
 
-  f32x4_t acc[TN];
-#pragma unroll
-  for (int t = 0; t < TN; t++) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   for (int it = 0; it < niter; it++) {
     const uint32_t k0 = kbase + (uint32_t)(it * KCH);
     // x staging: row r, 16-byte chunk `lane` of the KCH-wide slice (KCH/8 chunks <= 64)
     u32x4_t xst[4];
-    if constexpr (XLDS) {
 #pragma unroll
-      for (int r = 0; r < 4; r++)
-        if (r < M && lane < KCH / 8) xst[r] = bld16(rx, (uint32_t)(r * (uint32_t)K + k0 + 8 * lane) * 2);
+    for (int r = 0; r < 4; r++)
+      if (r < M && lane < KCH / 8) xst[r] = bld16(rx, (uint32_t)(r * (uint32_t)K + k0 + 8 * lane) * 2);
+    scale_t<WDT> sv[NSTEP];
+    u32x4_t wr[NSTEP];
+#pragma unroll
+    for (int c = 0; c < NSTEP; c++) {
+      const uint32_t kk = k0 + c * KSTEP + EPL * g;
+      sv[c] = scale_of<WDT>(rs, (uint32_t)nl * spr + (kk >> gs));
     }
-    scale_t<WDT> sv[NSTEP][TN];
-    u32x4_t wr[NSTEP][TN];
 #pragma unroll
-    for (int c = 0; c < NSTEP; c++)
-#pragma unroll
-      for (int t = 0; t < TN; t++) {
-        const uint32_t kk = k0 + c * KSTEP + EPL * g;
-        sv[c][t] = scale_of<WDT>(rs, (uint32_t)(16 * t + nl) * spr + (kk >> gs));
-      }
-#pragma unroll
-    for (int c = 0; c < NSTEP; c++)
-#pragma unroll
-      for (int t = 0; t < TN; t++) {
-        const uint32_t kk = k0 + c * KSTEP + EPL * g;
-        wr[c][t] = bld16(rw, (uint32_t)(16 * t + nl) * rowbytes + kk * BPE2 / 2);
-      }
-    if constexpr (XLDS) {
-#pragma unroll
-      for (int r = 0; r < 4; r++)
-        if (r < M && lane < KCH / 8) *reinterpret_cast<u32x4_t*>(xw + (r * KCH + 8 * lane) * 2) = xst[r];
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int c = 0; c < NSTEP; c++) {
+      const uint32_t kk = k0 + c * KSTEP + EPL * g;
+      wr[c] = bld16(rw, (uint32_t)nl * rowbytes + kk * BPE2 / 2);
     }
+#pragma unroll
+    for (int r = 0; r < 4; r++)
+      if (r < M && lane < KCH / 8) *reinterpret_cast<u32x4_t*>(xw + (r * KCH + 8 * lane) * 2) = xst[r];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int c = 0; c < NSTEP; c++) {
       bf16x8_t xa[MF];
 #pragma unroll
       for (int j = 0; j < MF; j++) {
         const uint32_t kl = c * KSTEP + EPL * g + 8 * j;       // k within the chunk
-        if constexpr (XLDS) {
-          const uint32_t off = nl < M ? (nl * KCH + kl) * 2 : 4 * KCH * 2;
-          xa[j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(xw + off));
-        } else {
-          xa[j] = as_bf16x8(bld16(rx, (nl * (uint32_t)K + k0 + kl) * 2));
-        }
+        const uint32_t off = nl < M ? (nl * KCH + kl) * 2 : 4 * KCH * 2;
+        xa[j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(xw + off));
       }
+      bf16x8_t b[4];
+      dequant16<WDT>(wr[c], sv[c], b);
 #pragma unroll
-      for (int t = 0; t < TN; t++) {
-        bf16x8_t b[4];
-        dequant16<WDT>(wr[c][t], sv[c][t], b);
-#pragma unroll
-        for (int j = 0; j < MF; j++) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[j], b[j], acc[t], 0, 0, 0);
-      }
+      for (int j = 0; j < MF; j++) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[j], b[j], acc, 0, 0, 0);
     }
-    if constexpr (XLDS) {
-      // the next chunk's staging overwrites this wave's region
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
+    // the next chunk's staging overwrites this wave's region
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
-  // acc[t][i] holds C[m = 4g + i][n = nl] of tile t.
+  // acc[i] holds C[m = 4g + i][n = nl].
 #pragma unroll
-  for (int t = 0; t < TN; t++)
-#pragma unroll
-    for (int i = 0; i < 4; i++) red[((wave * TN + t) * 16 + 4 * g + i) * 16 + nl] = acc[t][i];
+  for (int i = 0; i < 4; i++) red[(wave * 16 + 4 * g + i) * 16 + nl] = acc[i];
   __syncthreads();
-  for (int idx = threadIdx.x; idx < TN * 256; idx += blockDim.x) {
-    const int t = idx >> 8, m = (idx >> 4) & 15, n = idx & 15;
-    const int64_t col = n0 + 16 * t + n;
+  for (int idx = threadIdx.x; idx < 256; idx += blockDim.x) {
+    const int m = idx >> 4, n = idx & 15;
+    const int64_t col = n0 + n;
     if (m >= M || col >= N) continue;
     float s = 0.0f;
-    for (int wv = 0; wv < S; wv++) s += red[((wv * TN + t) * 16 + m) * 16 + n];
+    for (int wv = 0; wv < S; wv++) s += red[(wv * 16 + m) * 16 + n];
     s *= WDT == W_FP8 ? chscale[col] * alpha : alpha;
     y[(int64_t)m * N + col] = (uint16_t)f32_to_bf16_bits(s);
   }
 }
 
-// 4 < M <= 16, one 16-column tile per workgroup: each chunk's x rows are
-// fetched whole (consecutive lanes read consecutive 16-byte pieces of a row)
+// 4 < M <= 16, TN (one or two) 16-column tiles per workgroup: each chunk's x
+// rows are fetched whole (consecutive lanes read consecutive 16-byte pieces of a row)
 // and pass through the wave's LDS region, piece p of row r at p ^ (r & 15), so
 // that the 16 rows of one fragment read sit in distinct banks.  Read straight
 // into the MFMA layout instead, a lane's four pieces of a row lie 64 bytes
@@ -269,7 +245,7 @@ __global__ __launch_bounds__(1024) void k_gemv(const uint16_t* __restrict__ x, i
 // wave's last chunk, and an x row past M, load from an offset outside the
 // buffer range, which returns zeros without a memory access, so every load is
 // issued unconditionally and the wait counts stay fixed).
-template <int WDT, int NSTEP>
+template <int WDT, int NSTEP, int TN>
 __global__ __launch_bounds__(1024) void k_gemv_x16(const uint16_t* __restrict__ x, int M, int64_t N, int64_t K,
                                                   const uint8_t* __restrict__ w, const void* __restrict__ sc,
                                                   int group_shift, const float* __restrict__ chscale, float alpha,
@@ -289,9 +265,9 @@ __global__ __launch_bounds__(1024) void k_gemv_x16(const uint16_t* __restrict__ 
   const int S = blockDim.x >> 6;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nl = lane & 15, g = lane >> 4;
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int64_t n0 = (int64_t)blockIdx.x * 16 * TN;
   const uint32_t rowbytes = (uint32_t)(K * BPE2 / 2);
-  const int64_t nrows = N - n0 < 16 ? N - n0 : 16;
+  const int64_t nrows = N - n0 < 16 * TN ? N - n0 : 16 * TN;
   const int gs = gshift_of<WDT>(group_shift);
   const uint32_t spr = (uint32_t)(K >> gs);
   const auto rw = make_rsrc(w + n0 * rowbytes, nrows * rowbytes);
@@ -307,8 +283,8 @@ __global__ __launch_bounds__(1024) void k_gemv_x16(const uint16_t* __restrict__ 
 
   struct Chunk {
     u32x4_t xs[XL];
-    u32x4_t wr[NSTEP];
-    uint32_t sv[NSTEP];                                     // raw bits, converted at the use
+    u32x4_t wr[NSTEP][TN];
+    uint32_t sv[NSTEP][TN];                                 // raw bits, converted at the use
   };
   auto issue = [&](Chunk& b, int it) {
     const bool ok = it < niter;
@@ -319,17 +295,23 @@ __global__ __launch_bounds__(1024) void k_gemv_x16(const uint16_t* __restrict__ 
       b.xs[i] = bld16(rx, ok && r < M ? (uint32_t)(r * (uint32_t)K + k0 + 8 * p) * 2 : OUT);
     }
 #pragma unroll
-    for (int c = 0; c < NSTEP; c++) {
-      const uint32_t kk = k0 + c * KSTEP + EPL * g;
-      b.sv[c] = scale_raw_of<WDT>(rs, ok ? (uint32_t)nl * spr + (kk >> gs) : SOUT);
-    }
+    for (int c = 0; c < NSTEP; c++)
 #pragma unroll
-    for (int c = 0; c < NSTEP; c++) {
-      const uint32_t kk = k0 + c * KSTEP + EPL * g;
-      b.wr[c] = bld16(rw, ok ? (uint32_t)nl * rowbytes + kk * BPE2 / 2 : OUT);
-    }
+      for (int t = 0; t < TN; t++) {
+        const uint32_t kk = k0 + c * KSTEP + EPL * g;
+        b.sv[c][t] = scale_raw_of<WDT>(rs, ok ? (uint32_t)(16 * t + nl) * spr + (kk >> gs) : SOUT);
+      }
+#pragma unroll
+    for (int c = 0; c < NSTEP; c++)
+#pragma unroll
+      for (int t = 0; t < TN; t++) {
+        const uint32_t kk = k0 + c * KSTEP + EPL * g;
+        b.wr[c][t] = bld16(rw, ok ? (uint32_t)(16 * t + nl) * rowbytes + kk * BPE2 / 2 : OUT);
+      }
   };
-  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t acc[TN];
+#pragma unroll
+  for (int t = 0; t < TN; t++) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   auto consume = [&](Chunk& b) {
     // the previous chunk's fragment reads of the region come first
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -351,10 +333,13 @@ __global__ __launch_bounds__(1024) void k_gemv_x16(const uint16_t* __restrict__ 
         const int p = (c * KSTEP + EPL * g + 8 * j) >> 3;
         xa[j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(xw + xtr * XRB + ((p ^ (xtr & 15)) << 4)));
       }
-      bf16x8_t bq[4];
-      dequant16<WDT>(b.wr[c], scale_from_raw<WDT>(b.sv[c]), bq);
 #pragma unroll
-      for (int j = 0; j < MF; j++) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[j], bq[j], acc, 0, 0, 0);
+      for (int t = 0; t < TN; t++) {
+        bf16x8_t bq[4];
+        dequant16<WDT>(b.wr[c][t], scale_from_raw<WDT>(b.sv[c][t]), bq);
+#pragma unroll
+        for (int j = 0; j < MF; j++) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[j], bq[j], acc[t], 0, 0, 0);
+      }
     }
   };
   Chunk ca, cb;
@@ -366,16 +351,18 @@ __global__ __launch_bounds__(1024) void k_gemv_x16(const uint16_t* __restrict__ 
     if (it + 1 < niter) consume(cb);
   }
 
-  // acc[i] holds C[m = 4g + i][n = nl]
+  // acc[t][i] holds C[m = 4g + i][n = nl] of tile t
 #pragma unroll
-  for (int i = 0; i < 4; i++) red[(wave * 16 + 4 * g + i) * 16 + nl] = acc[i];
+  for (int t = 0; t < TN; t++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) red[((wave * TN + t) * 16 + 4 * g + i) * 16 + nl] = acc[t][i];
   __syncthreads();
-  for (int idx = threadIdx.x; idx < 256; idx += blockDim.x) {
-    const int m = idx >> 4, n = idx & 15;
-    const int64_t col = n0 + n;
+  for (int idx = threadIdx.x; idx < TN * 256; idx += blockDim.x) {
+    const int t = idx >> 8, m = (idx >> 4) & 15, n = idx & 15;
+    const int64_t col = n0 + 16 * t + n;
     if (m >= M || col >= N) continue;
     float s = 0.0f;
-    for (int wv = 0; wv < S; wv++) s += red[(wv * 16 + m) * 16 + n];
+    for (int wv = 0; wv < S; wv++) s += red[((wv * TN + t) * 16 + m) * 16 + n];
     s *= WDT == W_FP8 ? chscale[col] * alpha : alpha;
     y[(int64_t)m * N + col] = (uint16_t)f32_to_bf16_bits(s);
   }
@@ -990,42 +977,42 @@ inline GemvSplit gemv_split(int64_t T, int maxstep, int smax) {
   return GemvSplit{ns, (int)(chunks < smax ? chunks : smax), (int)chunks};
 }
 
-template <int WDT, int TN, int NSTEP, bool XLDS>
+template <int WDT, int NSTEP>
 hipError_t gemv_go(const GemvSplit& sp, const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w,
              const void* sc, int group, const float* ch, float alpha, uint16_t* y, hipStream_t s) {
-  const unsigned grid = (unsigned)((N + 16 * TN - 1) / (16 * TN));
-  constexpr int KCH = NSTEP * (WTraits<WDT>::bits == 4 ? 128 : 64);
-  const size_t lds = (XLDS ? (size_t)sp.S * (4 * KCH * 2 + 64) : 0) + (size_t)sp.S * TN * 1024;
-  const int gshift = group == 32 ? 5 : group == 64 ? 6 : 7;
-  const hipError_t e = allow_lds<k_gemv<WDT, TN, NSTEP, XLDS>>(lds);
-  if (e != hipSuccess) return e;
-  k_gemv<WDT, TN, NSTEP, XLDS><<<grid, 64 * sp.S, lds, s>>>(x, (int)M, N, K, w, sc, gshift, ch, alpha, y, sp.nchunk);
-  return hipSuccess;
-}
-
-template <int WDT, int NSTEP>
-hipError_t x16_go(const GemvSplit& sp, const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w,
-                  const void* sc, int group, const float* ch, float alpha, uint16_t* y, hipStream_t s) {
   const unsigned grid = (unsigned)((N + 15) / 16);
   constexpr int KCH = NSTEP * (WTraits<WDT>::bits == 4 ? 128 : 64);
-  const size_t lds = (size_t)sp.S * (16 * KCH * 2 + 1024);
+  const size_t lds = (size_t)sp.S * (4 * KCH * 2 + 64) + (size_t)sp.S * 1024;
   const int gshift = group == 32 ? 5 : group == 64 ? 6 : 7;
-  const hipError_t e = allow_lds<k_gemv_x16<WDT, NSTEP>>(lds);
+  const hipError_t e = allow_lds<k_gemv<WDT, NSTEP>>(lds);
   if (e != hipSuccess) return e;
-  k_gemv_x16<WDT, NSTEP><<<grid, 64 * sp.S, lds, s>>>(x, (int)M, N, K, w, sc, gshift, ch, alpha, y, sp.nchunk);
+  k_gemv<WDT, NSTEP><<<grid, 64 * sp.S, lds, s>>>(x, (int)M, N, K, w, sc, gshift, ch, alpha, y, sp.nchunk);
   return hipSuccess;
 }
 
-template <int WDT, int TN, bool XLDS>
+template <int WDT>
 hipError_t gemv_nstep(const GemvSplit& sp, const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w,
                       const void* sc, int group, const float* ch, float alpha, uint16_t* y, hipStream_t s) {
   switch (sp.nstep) {
-    case 8: if constexpr (WTraits<WDT>::bits == 8) return gemv_go<WDT, TN, 8, XLDS>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s);
+    case 8: if constexpr (WTraits<WDT>::bits == 8) return gemv_go<WDT, 8>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s);
             [[fallthrough]];
-    case 4: return gemv_go<WDT, TN, 4, XLDS>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s);
-    case 2: return gemv_go<WDT, TN, 2, XLDS>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s);
-    default: return gemv_go<WDT, TN, 1, XLDS>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s);
+    case 4: return gemv_go<WDT, 4>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s);
+    case 2: return gemv_go<WDT, 2>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s);
+    default: return gemv_go<WDT, 1>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s);
   }
+}
+
+template <int WDT, int NSTEP, int TN = 1>
+hipError_t x16_go(const GemvSplit& sp, const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w,
+                  const void* sc, int group, const float* ch, float alpha, uint16_t* y, hipStream_t s) {
+  const unsigned grid = (unsigned)((N + 16 * TN - 1) / (16 * TN));
+  constexpr int KCH = NSTEP * (WTraits<WDT>::bits == 4 ? 128 : 64);
+  const size_t lds = (size_t)sp.S * (16 * KCH * 2 + TN * 1024);
+  const int gshift = group == 32 ? 5 : group == 64 ? 6 : 7;
+  const hipError_t e = allow_lds<k_gemv_x16<WDT, NSTEP, TN>>(lds);
+  if (e != hipSuccess) return e;
+  k_gemv_x16<WDT, NSTEP, TN><<<grid, 64 * sp.S, lds, s>>>(x, (int)M, N, K, w, sc, gshift, ch, alpha, y, sp.nchunk);
+  return hipSuccess;
 }
 
 // 4 < M <= 16: the 16 x rows of the wave's slice do not fit a wave's LDS
@@ -1399,7 +1386,8 @@ bool ring_path(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t
     case 2: st = ring16_go<WDT, 2, GSH>(M, x, N, K, w, sc, ch, alpha, y, s); return true;
     case 4: st = ring16_go<WDT, 4, GSH>(M, x, N, K, w, sc, ch, alpha, y, s); return true;
     case 8: st = ring16_go<WDT, 8, GSH>(M, x, N, K, w, sc, ch, alpha, y, s); return true;
-    case 16: st = ring16_go<WDT, 16, GSH>(M, x, N, K, w, sc, ch, alpha, y, s); return true;
+    // (longer K: two tiles per workgroup with x through LDS measured faster,
+    // N = 8192, K = 8192: 16.0 -> 14.7 us at M = 5 and 8)
     default: return false;
   }
 }
@@ -1425,27 +1413,28 @@ wq_status launch_gemv(const uint16_t* x, int64_t M, int64_t N, int64_t K, const 
     // K = 128*j with j odd only matters for 8-bit weights, whose step is 64: always divisible
     return WQ_EINVAL;
   }
-  // up to 16 waves per workgroup when the column tiles alone do not fill the
-  // CUs; two 16-column tiles per workgroup for M > 4 only when there are
-  // enough of them
+  // up to 16 waves per workgroup when the column tiles alone do not fill the CUs
   int ncu = 0;
   if (cu_count(&ncu) != hipSuccess) return WQ_EHIP;
   const int64_t tiles = (N + 15) / 16;
-  const bool two = M > 4 && tiles >= 4 * (int64_t)ncu;
-  const GemvSplit sp = gemv_split(K / KSTEP, MAXSTEP, (two ? tiles / 2 : tiles) <= ncu ? 16 : 8);
   hipError_t e;
-  if (M <= 4) e = gemv_nstep<WDT, 1, true>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s);
-  else if (!two) {
-    // x through LDS; a chunk row's 16-byte x pieces come in groups of 16
-    // (one step for 4-bit weights, two for 8-bit, whose step count is even
-    // since K % 128 == 0; one step measured faster than two for 4-bit,
-    // N = 1792-8192, K = 4096-14336, M = 5-16)
+  if (M <= 4) {
+    e = gemv_nstep<WDT>(gemv_split(K / KSTEP, MAXSTEP, tiles <= ncu ? 16 : 8), x, M, N, K, w, sc, group, ch, alpha,
+                        y, s);
+  } else {
+    // x through LDS, one chunk row's 16-byte x pieces in groups of 16 (one
+    // step for 4-bit weights, two for 8-bit: their step count is even since
+    // K % 128 == 0; one step measured faster than two for 4-bit, N = 1792-8192,
+    // K = 4096-14336, M = 5-16).  Two 16-column tiles per workgroup when the
+    // tiles outnumber the CUs, so that x is fetched once per 32 columns
+    // (N = 8192, K = 14336, M = 16: 29.6 -> 25.5 us).
     constexpr int XS = WTraits<WDT>::bits == 4 ? 1 : 2;
-    const GemvSplit sx = gemv_split(K / KSTEP, XS, tiles <= ncu ? 16 : 8);
-    e = sx.nstep == XS ? x16_go<WDT, XS>(sx, x, M, N, K, w, sc, group, ch, alpha, y, s)
-                       : gemv_nstep<WDT, 1, false>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s);
+    const bool t2 = tiles > ncu;
+    const GemvSplit sx = gemv_split(K / KSTEP, XS, (t2 ? (tiles + 1) / 2 : tiles) <= ncu ? 16 : 8);
+    if (sx.nstep != XS) return WQ_EINVAL;
+    e = t2 ? x16_go<WDT, XS, 2>(sx, x, M, N, K, w, sc, group, ch, alpha, y, s)
+           : x16_go<WDT, XS, 1>(sx, x, M, N, K, w, sc, group, ch, alpha, y, s);
   }
-  else e = gemv_nstep<WDT, 2, false>(sp, x, M, N, K, w, sc, group, ch, alpha, y, s);
   return e != hipSuccess ? WQ_EHIP : wq_launch_status();
 }
 
