@@ -266,9 +266,9 @@ wq_status wq_dequant(const void* wq, int w_dtype, const void* w_scales, int s_dt
  *         per-tensor scale of NVFP4; 1 otherwise).  Non-finite: WQ_EINVAL.
  *         y = bf16(acc * RN(chan * alpha)) for WQ_E4M3 weights,
  *         y = bf16(acc * alpha) for the others.
- * M >= 1, N >= 1, K % 128 == 0.  M <= 16 runs the split-K decode kernels;
- * 16 < M <= 64 runs them once per group of 16 rows (one launch each, all on
- * `stream`); larger M the MFMA prefill kernel.
+ * M >= 1, N >= 1, K % 128 == 0.  M <= 32 runs the split-K decode kernels;
+ * 32 < M <= 64 runs them twice, on rows 0-31 and on the rest (both launches
+ * on `stream`); larger M the MFMA prefill kernel.
  * workspace / ws_bytes: reserved; the current kernels need none
  * (wq_gemm_workspace_size returns 0) and accept NULL / 0.
  * Accuracy contract: |y - y_ref| <= 8e-3 |y_ref| + 1e-3 sum_k |x_k w_k| per

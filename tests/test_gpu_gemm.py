@@ -279,6 +279,23 @@ def test_gemv_few_tiles_5_to_16(W, kind, M, N, K):
 
 
 @pytest.mark.parametrize("kind", ["int4", "mxfp4", "e4m3"])
+@pytest.mark.parametrize("M", [17, 25, 32, 40, 64])
+@pytest.mark.parametrize("N,K", [(1000, 2048), (4500, 1152)])
+def test_gemv_32_rows(W, kind, M, N, K):
+    # 16 < M <= 64 in launches of up to 32 rows: two 16-row groups share every
+    # converted weight fragment, one 16-column tile per workgroup (N = 1000) or
+    # two with at most 8 waves (N = 4500, ragged last workgroup); M = 40 and 64
+    # take a second launch of 8 and 32 rows
+    g = np.random.default_rng(990 + M * 3 + N + K)
+    Wf = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
+    Wf[:, g.choice(K, 5, replace=False)] *= 30
+    xbits = to_bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    args, wdeq, chan = _prep(W, kind, Wf)
+    banner("gemv 32 rows", kind, M, N, K)
+    _check(W.wq_gemm(dev_bf16(xbits), *args, N), xbits, wdeq, chan)
+
+
+@pytest.mark.parametrize("kind", ["int4", "mxfp4", "e4m3"])
 @pytest.mark.parametrize("M", [5, 11, 16])
 @pytest.mark.parametrize("N,K", [(300, 14336), (70, 1152), (4500, 1536), (40, 640), (4100, 8192)])
 def test_gemv_x_through_lds(W, kind, M, N, K):

@@ -245,8 +245,8 @@ __global__ __launch_bounds__(1024) void k_gemv(const uint16_t* __restrict__ x, i
 // wave's last chunk, and an x row past M, load from an offset outside the
 // buffer range, which returns zeros without a memory access, so every load is
 // issued unconditionally and the wait counts stay fixed).
-template <int WDT, int NSTEP, int TN>
-__global__ __launch_bounds__(1024) void k_gemv_x16(const uint16_t* __restrict__ x, int M, int64_t N, int64_t K,
+template <int WDT, int NSTEP, int TN, int MG>
+__global__ __launch_bounds__(TN * MG >= 4 ? 512 : 1024) void k_gemv_x16(const uint16_t* __restrict__ x, int M, int64_t N, int64_t K,
                                                   const uint8_t* __restrict__ w, const void* __restrict__ sc,
                                                   int group_shift, const float* __restrict__ chscale, float alpha,
                                                   uint16_t* __restrict__ y, int nchunk) {
@@ -257,9 +257,11 @@ __global__ __launch_bounds__(1024) void k_gemv_x16(const uint16_t* __restrict__ 
   constexpr int BPE2 = WTraits<WDT>::bits == 4 ? 1 : 2;     // bytes per 2 elements
   constexpr int SB = scale_bytes<WDT>();
   constexpr int XCH = KCH / 8;                              // 16-byte pieces per x row of a chunk
-  constexpr int XL = 16 * XCH / 64;                         // x loads per lane per chunk
+  constexpr int XL = 16 * MG * XCH / 64;                    // x loads per lane per chunk
   constexpr int XRB = KCH * 2;                              // bytes per x row of a chunk
+  constexpr int XWB = 16 * MG * XRB;                        // per-wave x region
   static_assert(XCH % 16 == 0 && XCH <= 64, "x pieces are swizzled in groups of 16");
+  static_assert(TN * MG * 1024 <= XWB, "the partial sums reuse the wave's x region");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int S = blockDim.x >> 6;
@@ -277,9 +279,7 @@ __global__ __launch_bounds__(1024) void k_gemv_x16(const uint16_t* __restrict__ 
   const int c0 = (int)((int64_t)wave * nchunk / S), niter = (int)((int64_t)(wave + 1) * nchunk / S) - c0;
   constexpr uint32_t OUT = 0x7FFFFFF0u;                     // past every range (all <= this many bytes)
   constexpr uint32_t SOUT = OUT / 4;                        // scale index past every scale range
-  uint8_t* xw = smem + wave * 16 * XRB;
-  float* red = reinterpret_cast<float*>(smem + S * 16 * XRB);
-  const int xtr = nl < M ? nl : 0;                          // rows past M read row 0; dropped
+  uint8_t* xw = smem + wave * XWB;
 
   struct Chunk {
     u32x4_t xs[XL];
@@ -309,9 +309,11 @@ __global__ __launch_bounds__(1024) void k_gemv_x16(const uint16_t* __restrict__ 
         b.wr[c][t] = bld16(rw, ok ? (uint32_t)(16 * t + nl) * rowbytes + kk * BPE2 / 2 : OUT);
       }
   };
-  f32x4_t acc[TN];
+  f32x4_t acc[MG][TN];
 #pragma unroll
-  for (int t = 0; t < TN; t++) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < MG; q++)
+#pragma unroll
+    for (int t = 0; t < TN; t++) acc[q][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   auto consume = [&](Chunk& b) {
     // the previous chunk's fragment reads of the region come first
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -327,18 +329,25 @@ __global__ __launch_bounds__(1024) void k_gemv_x16(const uint16_t* __restrict__ 
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int c = 0; c < NSTEP; c++) {
-      bf16x8_t xa[MF];
+      bf16x8_t xa[MG][MF];
 #pragma unroll
-      for (int j = 0; j < MF; j++) {
-        const int p = (c * KSTEP + EPL * g + 8 * j) >> 3;
-        xa[j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(xw + xtr * XRB + ((p ^ (xtr & 15)) << 4)));
+      for (int q = 0; q < MG; q++) {
+        const int row = 16 * q + nl, xr = row < M ? row : 0;  // rows past M read row 0; dropped
+#pragma unroll
+        for (int j = 0; j < MF; j++) {
+          const int p = (c * KSTEP + EPL * g + 8 * j) >> 3;
+          xa[q][j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(xw + xr * XRB + ((p ^ (xr & 15)) << 4)));
+        }
       }
 #pragma unroll
       for (int t = 0; t < TN; t++) {
         bf16x8_t bq[4];
         dequant16<WDT>(b.wr[c][t], scale_from_raw<WDT>(b.sv[c][t]), bq);
 #pragma unroll
-        for (int j = 0; j < MF; j++) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[j], bq[j], acc[t], 0, 0, 0);
+        for (int q = 0; q < MG; q++)
+#pragma unroll
+          for (int j = 0; j < MF; j++)
+            acc[q][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[q][j], bq[j], acc[q][t], 0, 0, 0);
       }
     }
   };
@@ -351,18 +360,25 @@ __global__ __launch_bounds__(1024) void k_gemv_x16(const uint16_t* __restrict__ 
     if (it + 1 < niter) consume(cb);
   }
 
-  // acc[t][i] holds C[m = 4g + i][n = nl] of tile t
+  // acc[q][t][i] holds C[m = 16q + 4g + i][n = nl] of tile t; the partial
+  // sums go to the front of the wave's own x region once its reads are done
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float* red = reinterpret_cast<float*>(xw);
 #pragma unroll
-  for (int t = 0; t < TN; t++)
+  for (int q = 0; q < MG; q++)
 #pragma unroll
-    for (int i = 0; i < 4; i++) red[((wave * TN + t) * 16 + 4 * g + i) * 16 + nl] = acc[t][i];
+    for (int t = 0; t < TN; t++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) red[((q * TN + t) * 16 + 4 * g + i) * 16 + nl] = acc[q][t][i];
   __syncthreads();
-  for (int idx = threadIdx.x; idx < TN * 256; idx += blockDim.x) {
-    const int t = idx >> 8, m = (idx >> 4) & 15, n = idx & 15;
+  for (int idx = threadIdx.x; idx < MG * TN * 256; idx += blockDim.x) {
+    const int qt = idx >> 8, q = qt / TN, t = qt % TN, m = 16 * q + ((idx >> 4) & 15), n = idx & 15;
     const int64_t col = n0 + 16 * t + n;
     if (m >= M || col >= N) continue;
     float s = 0.0f;
-    for (int wv = 0; wv < S; wv++) s += red[((wv * TN + t) * 16 + m) * 16 + n];
+    for (int wv = 0; wv < S; wv++) s += reinterpret_cast<const float*>(smem + wv * XWB)[idx];
     s *= WDT == W_FP8 ? chscale[col] * alpha : alpha;
     y[(int64_t)m * N + col] = (uint16_t)f32_to_bf16_bits(s);
   }
@@ -1002,16 +1018,17 @@ hipError_t gemv_nstep(const GemvSplit& sp, const uint16_t* x, int64_t M, int64_t
   }
 }
 
-template <int WDT, int NSTEP, int TN = 1>
+template <int WDT, int NSTEP, int TN, int MG>
 hipError_t x16_go(const GemvSplit& sp, const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w,
                   const void* sc, int group, const float* ch, float alpha, uint16_t* y, hipStream_t s) {
   const unsigned grid = (unsigned)((N + 16 * TN - 1) / (16 * TN));
   constexpr int KCH = NSTEP * (WTraits<WDT>::bits == 4 ? 128 : 64);
-  const size_t lds = (size_t)sp.S * (16 * KCH * 2 + TN * 1024);
+  const size_t lds = (size_t)sp.S * 16 * MG * KCH * 2;
   const int gshift = group == 32 ? 5 : group == 64 ? 6 : 7;
-  const hipError_t e = allow_lds<k_gemv_x16<WDT, NSTEP, TN>>(lds);
+  const hipError_t e = allow_lds<k_gemv_x16<WDT, NSTEP, TN, MG>>(lds);
   if (e != hipSuccess) return e;
-  k_gemv_x16<WDT, NSTEP, TN><<<grid, 64 * sp.S, lds, s>>>(x, (int)M, N, K, w, sc, gshift, ch, alpha, y, sp.nchunk);
+  k_gemv_x16<WDT, NSTEP, TN, MG><<<grid, 64 * sp.S, lds, s>>>(x, (int)M, N, K, w, sc, gshift, ch, alpha, y,
+                                                             sp.nchunk);
   return hipSuccess;
 }
 
@@ -1267,8 +1284,10 @@ __global__ __launch_bounds__(64 * WW) __attribute__((amdgpu_waves_per_eu(WW / 4,
 // ring beat deeper rings (requests all in flight arrive in an order that
 // bunches the dequantization work at the end) and 8-wave splits.
 constexpr int RING_NW = 4;
-// row groups of 16 that wq_gemm sends through the decode forms (16 < M <= 64)
-constexpr int WQ_DECODE_GROUPS = 4;
+// M up to WQ_DECODE_ROWS runs the decode forms, in launches of up to
+// WQ_GROUP_ROWS rows (17-32 rows share each converted weight fragment between
+// two 16-row MFMA groups)
+constexpr int WQ_DECODE_ROWS = 64, WQ_GROUP_ROWS = 32;
 constexpr int RING_DEPTH = 2;
 // 4 < M <= 16: two 16-column tiles per workgroup share every x chunk, which
 // halves the x traffic from L2 (each workgroup reads the whole x slice).
@@ -1372,6 +1391,7 @@ bool ring_path(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t
   // when the 16-column tiles alone do not fill the CUs, the general form
   // (one tile and up to 16 waves per workgroup) is faster for 4 < M <= 16
   // (measured N = 1024-4096: 7.9-8.9 us against 11.3-12.1 us)
+  if (M > 16) return false;
   int ncu = 0;
   if (cu_count(&ncu) != hipSuccess) {
     st = WQ_EHIP;
@@ -1430,10 +1450,17 @@ wq_status launch_gemv(const uint16_t* x, int64_t M, int64_t N, int64_t K, const 
     // (N = 8192, K = 14336, M = 16: 29.6 -> 25.5 us).
     constexpr int XS = WTraits<WDT>::bits == 4 ? 1 : 2;
     const bool t2 = tiles > ncu;
-    const GemvSplit sx = gemv_split(K / KSTEP, XS, (t2 ? (tiles + 1) / 2 : tiles) <= ncu ? 16 : 8);
+    // (two tiles and 32 rows need more than 128 registers per lane: at most 8
+    // waves per workgroup)
+    const bool s16 = (t2 ? (tiles + 1) / 2 : tiles) <= ncu && !(t2 && M > 16);
+    const GemvSplit sx = gemv_split(K / KSTEP, XS, s16 ? 16 : 8);
     if (sx.nstep != XS) return WQ_EINVAL;
-    e = t2 ? x16_go<WDT, XS, 2>(sx, x, M, N, K, w, sc, group, ch, alpha, y, s)
-           : x16_go<WDT, XS, 1>(sx, x, M, N, K, w, sc, group, ch, alpha, y, s);
+    if (M > 16)
+      e = t2 ? x16_go<WDT, XS, 2, 2>(sx, x, M, N, K, w, sc, group, ch, alpha, y, s)
+             : x16_go<WDT, XS, 1, 2>(sx, x, M, N, K, w, sc, group, ch, alpha, y, s);
+    else
+      e = t2 ? x16_go<WDT, XS, 2, 1>(sx, x, M, N, K, w, sc, group, ch, alpha, y, s)
+             : x16_go<WDT, XS, 1, 1>(sx, x, M, N, K, w, sc, group, ch, alpha, y, s);
   }
   return e != hipSuccess ? WQ_EHIP : wq_launch_status();
 }
@@ -1482,11 +1509,12 @@ wq_status wq_gemm(const void* x_bf16, int64_t M, int64_t N, int64_t K, const voi
   const float* ch = wdt == W_FP8 ? (const float*)w_scales : nullptr;
   // M <= 16: the decode forms.  16 < M <= 64: the GEMM's 256-row tiles leave
   // most CUs idle (N / 256 workgroups: 90 us at N = 14336, K = 4096 for any
-  // M up to 512), so the rows go through the decode forms in groups of 16,
-  // each launch streaming the weights once (about 13 us per group there).
-  if (M <= WQ_DECODE_GROUPS * 16) {
-    for (int64_t m0 = 0; m0 < M; m0 += 16) {
-      const int64_t mg = M - m0 < 16 ? M - m0 : 16;
+  // M up to 512), so the rows go through the decode forms in launches of up
+  // to 32 rows, each streaming the weights once (about 20 us per 32 rows
+  // there).
+  if (M <= WQ_DECODE_ROWS) {
+    for (int64_t m0 = 0; m0 < M; m0 += WQ_GROUP_ROWS) {
+      const int64_t mg = M - m0 < WQ_GROUP_ROWS ? M - m0 : WQ_GROUP_ROWS;
       const uint16_t* xg = x + m0 * K;
       uint16_t* yg = y + m0 * N;
       wq_status st;
