@@ -268,7 +268,10 @@ wq_status wq_dequant(const void* wq, int w_dtype, const void* w_scales, int s_dt
  *         y = bf16(acc * alpha) for the others.
  * M >= 1, N >= 1, K % 128 == 0.  M <= 32 runs the split-K decode kernels;
  * 32 < M <= 64 runs them twice, on rows 0-31 and on the rest (both launches
- * on `stream`); larger M the MFMA prefill kernel.
+ * on `stream`); larger M the MFMA prefill kernel, except that for
+ * 64 < M <= 256 the decode launches (one per 32 rows) are taken when a cost
+ * estimate from M, N, K and the CU count puts them ahead (at small N the
+ * prefill kernel's 256 x 256 tiles leave most CUs idle).
  * workspace / ws_bytes: reserved; the current kernels need none
  * (wq_gemm_workspace_size returns 0) and accept NULL / 0.
  * Accuracy contract: |y - y_ref| <= 8e-3 |y_ref| + 1e-3 sum_k |x_k w_k| per

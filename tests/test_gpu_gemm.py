@@ -150,10 +150,11 @@ def test_decode_repeatable_with_cached_weights(W, decode_weights, M):
 
 
 @pytest.mark.parametrize("kind", ["int4", "mxfp4", "e4m3"])
-@pytest.mark.parametrize("M", [20, 33, 64, 65])
+@pytest.mark.parametrize("M", [20, 33, 64, 65, 100, 256])
 def test_gemm_row_groups(W, kind, M):
-    # 16 < M <= 64 runs the decode forms once per group of 16 rows (a last
-    # group of 4, 1 and 16 rows); M = 65 takes the prefill GEMM
+    # 16 < M <= 64 runs the decode forms in launches of up to 32 rows (a last
+    # launch of 1 and 32 rows); at this small N the decode launches also win
+    # up to M = 256 (3, 4 and 8 launches, the last of 1, 4 and 32 rows)
     N, K = 1000, 2048
     g = np.random.default_rng(1500 + M)
     Wf = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
@@ -161,6 +162,21 @@ def test_gemm_row_groups(W, kind, M):
     xbits = to_bf16_bits(g.standard_normal((M, K)).astype(np.float32))
     args, wdeq, chan = _prep(W, kind, Wf)
     banner("gemm row groups", kind, M, N, K)
+    _check(W.wq_gemm(dev_bf16(xbits), *args, N), xbits, wdeq, chan)
+
+
+@pytest.mark.parametrize("kind", ["int4", "mxfp4", "e4m3"])
+@pytest.mark.parametrize("M,N,K", [(256, 9000, 256), (129, 20000, 128), (65, 30000, 128)])
+def test_gemm_mid_rows_prefill(W, kind, M, N, K):
+    # 64 < M <= 256 at large N and short K, where the prefill grid fills the
+    # CUs and the 256x256 kernel is the estimated faster path (ragged M tile
+    # of 256, 129 and 65 rows)
+    g = np.random.default_rng(1600 + M + N + K)
+    Wf = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
+    Wf[:, g.choice(K, 3, replace=False)] *= 30
+    xbits = to_bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    args, wdeq, chan = _prep(W, kind, Wf)
+    banner("gemm mid rows prefill", kind, M, N, K)
     _check(W.wq_gemm(dev_bf16(xbits), *args, N), xbits, wdeq, chan)
 
 

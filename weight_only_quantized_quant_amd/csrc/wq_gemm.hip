@@ -1288,6 +1288,18 @@ constexpr int RING_NW = 4;
 // WQ_GROUP_ROWS rows (17-32 rows share each converted weight fragment between
 // two 16-row MFMA groups)
 constexpr int WQ_DECODE_ROWS = 64, WQ_GROUP_ROWS = 32;
+// 64 < M <= 256: the prefill kernel runs ceil(M/256) ceil(N/256) workgroups of
+// one 256x256 tile, each taking about 22 ns per element of K (90 us at
+// K = 4096), in rounds of one workgroup per CU; the decode launches of 32 rows
+// stream the weights at about 1.5 TB/s each.  Rows go through the decode forms
+// when that estimate is the smaller (at small N and large K the prefill grid
+// leaves most CUs idle).
+inline bool decode_rows_pay(int64_t M, int64_t N, int64_t K, int bits, int ncu) {
+  const int64_t wgs = ((M + 255) / 256) * ((N + 255) / 256);
+  const double t_pre = (double)((wgs + ncu - 1) / ncu) * (double)K * 0.022;        // us
+  const double t_dec = (double)((M + 31) / 32) * (double)N * (double)K * bits / 8 / 1.5e6;
+  return t_dec < t_pre;
+}
 constexpr int RING_DEPTH = 2;
 // 4 < M <= 16: two 16-column tiles per workgroup share every x chunk, which
 // halves the x traffic from L2 (each workgroup reads the whole x slice).
@@ -1512,7 +1524,15 @@ wq_status wq_gemm(const void* x_bf16, int64_t M, int64_t N, int64_t K, const voi
   // M up to 512), so the rows go through the decode forms in launches of up
   // to 32 rows, each streaming the weights once (about 20 us per 32 rows
   // there).
-  if (M <= WQ_DECODE_ROWS) {
+  bool rows = M <= WQ_DECODE_ROWS;
+#ifndef WQ_OLD_RULE
+  if (!rows && M <= 256) {
+    int ncu = 0;
+    if (cu_count(&ncu) != hipSuccess) return WQ_EHIP;
+    rows = decode_rows_pay(M, N, K, wdt == W_FP8 ? 8 : 4, ncu);
+  }
+#endif
+  if (rows) {
     for (int64_t m0 = 0; m0 < M; m0 += WQ_GROUP_ROWS) {
       const int64_t mg = M - m0 < WQ_GROUP_ROWS ? M - m0 : WQ_GROUP_ROWS;
       const uint16_t* xg = x + m0 * K;
