@@ -49,6 +49,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 ROTATE_BYTES = 700e6           # > 2.5x the 256 MB Infinity Cache
+DECODE_KERNEL = "k_gemv_ring<INT4> (wq_gemm, M<=4 decode path)"
 
 
 def parse():
@@ -58,6 +59,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--only", default=None)
     p.add_argument("--reps", type=int, default=0, help="launches for --only (default per case)")
+    p.add_argument("--rounds", type=int, default=5, help="timed regions of --steps launches (median)")
     p.add_argument("--no-cpu", action="store_true")
     return p.parse_args()
 
@@ -87,7 +89,8 @@ def graph_of(torch, fns):
 
 
 def time_graph(torch, g, launches):
-    """HIP events on the current stream around one replay; ms per launch."""
+    """HIP events on the current stream around one replay; ms per launch
+    (secondary measurements; the headline uses time_region)."""
     torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
@@ -97,6 +100,61 @@ def time_graph(torch, g, launches):
     b.synchronize()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / launches
+
+
+class Region:
+    """Timed regions of exactly `launches` launches, each preceded by a bounded
+    busy kernel (wq_util_spin) on the same stream, so that the host submits the
+    region's launches while the device is still busy and the submission
+    latency stays off the clock: event a fires when the busy kernel ends, and
+    the first launch follows at once.  The busy kernel's iteration count is
+    sized from a measured rate to last about twice the host's submission time.
+    `rounds` regions are timed; ms per launch is their median."""
+
+    def __init__(self, torch, W, enqueue, launches, rounds=5):
+        self.torch, self.W, self.enqueue, self.launches, self.rounds = torch, W, enqueue, launches, rounds
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        W.wq_util_spin(20000)
+        b.record()
+        b.synchronize()
+        self.ms_per_iter = max(a.elapsed_time(b) / 20000, 1e-6)
+        t = time.perf_counter()
+        enqueue()                                   # untimed pass: host submission time
+        self.host_ms = (time.perf_counter() - t) * 1e3
+        torch.cuda.synchronize()
+        self.iters = int(min(max(2.0 * max(self.host_ms, 0.05) / self.ms_per_iter, 1000), 1 << 24))
+        self.windows = []
+
+    def run(self, sampler=None):
+        torch = self.torch
+        ms, covered = [], []
+        for _ in range(self.rounds):
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0 = time.perf_counter()
+            self.W.wq_util_spin(self.iters)
+            a.record()
+            self.enqueue()
+            b.record()
+            t1 = time.perf_counter()
+            b.synchronize()
+            t2 = time.perf_counter()
+            ms.append(a.elapsed_time(b) / self.launches)
+            # the busy kernel outlasted the submission when the host was done
+            # before the busy kernel's planned end
+            covered.append((t1 - t0) * 1e3 < self.iters * self.ms_per_iter)
+            self.windows.append((t0, t2))
+        self.ms_rounds = ms
+        self.covered = all(covered)
+        return float(np.median(ms))
+
+    def describe(self):
+        return {"rounds_us_per_launch": [round(m * 1e3, 3) for m in self.ms_rounds],
+                "median_of_rounds": len(self.ms_rounds), "launches_per_round": self.launches,
+                "busy_kernel_us": round(self.iters * self.ms_per_iter * 1e3, 1),
+                "host_submit_us": round(self.host_ms * 1e3, 1), "busy_kernel_covered_submission": self.covered}
 
 
 class ClockSampler:
@@ -110,7 +168,7 @@ class ClockSampler:
 
     def __init__(self, torch):
         import threading
-        self.files, self.samples = {}, {}
+        self.files, self.samples, self.stamped = {}, {}, {}
         self.stop_evt, self.thread = threading.Event(), None
         try:
             p = torch.cuda.get_device_properties(0)
@@ -141,14 +199,16 @@ class ClockSampler:
             for key, (f, scale) in self.files.items():
                 try:
                     with open(f) as fh:
-                        self.samples.setdefault(key, []).append(self._value(fh.read(), scale))
+                        v = self._value(fh.read(), scale)
+                    self.samples.setdefault(key, []).append(v)
+                    self.stamped.setdefault(key, []).append((time.perf_counter(), v))
                 except (OSError, ValueError, IndexError):
                     pass
-            self.stop_evt.wait(0.0005)
+            self.stop_evt.wait(0.00025)
 
     def __enter__(self):
         import threading
-        self.samples = {}
+        self.samples, self.stamped = {}, {}
         self.stop_evt.clear()
         if self.files:
             self.thread = threading.Thread(target=self._run, daemon=True)
@@ -163,8 +223,16 @@ class ClockSampler:
         return False
 
     def summary(self):
-        return {k: {"median": round(float(np.median(v)), 1), "max": round(float(np.max(v)), 1), "samples": len(v)}
+        return {k: {"median": round(float(np.median(v)), 1), "min": round(float(np.min(v)), 1),
+                    "max": round(float(np.max(v)), 1), "samples": len(v)}
                 for k, v in self.samples.items() if v} or None
+
+    def per_window(self, windows):
+        """Samples taken inside each (t0, t1) host window, per key."""
+        out = []
+        for t0, t1 in windows:
+            out.append({k: [round(v, 1) for t, v in sv if t0 <= t <= t1] for k, sv in self.stamped.items()})
+        return out
 
 
 def time_eager(torch, fn, reps, warm=3, rounds=3):
@@ -218,10 +286,30 @@ def nvfp4_tensor_scale(torch, w):
     return float(w.abs().max().item()) / (6.0 * 448.0)
 
 
+def packed_copy(torch, parts):
+    """One device byte buffer holding `parts` (contiguous tensors) back to back,
+    each at a 256-byte boundary; returns (buffer, views of the parts, bytes
+    used).  The weight copies of a decode workload live in such buffers, so
+    that one streaming read covers exactly their footprint."""
+    offs, o = [], 0
+    for t in parts:
+        offs.append(o)
+        o += (t.numel() * t.element_size() + 255) // 256 * 256
+    buf = torch.empty(o, dtype=torch.uint8, device="cuda")
+    views = []
+    for t, off in zip(parts, offs):
+        n = t.numel() * t.element_size()
+        v = buf[off:off + n].view(t.dtype).view(t.shape)
+        v.copy_(t)
+        views.append(v)
+    return buf, views, o
+
+
 class Decode:
     """x[M, 4096] . dequant(W[14336, 4096])^T, INT4 g128 (symmetric, or
     asymmetric with a zero-point), E4M3 per-channel or NVFP4 (E4M3 scale per
-    16, per-tensor fp32 scale)."""
+    16, per-tensor fp32 scale).  Each weight copy (codes, then scales) lives in
+    one buffer; the copies together exceed the 256 MB Infinity Cache."""
 
     def __init__(self, torch, W, M, kind="int4", K=4096, N=14336):
         from synthetic import decode_inputs
@@ -254,7 +342,12 @@ class Decode:
             self.meta = (W.WQ_E4M3, W.WQ_F32, K)
         del wdev
         ncopy = max(1, int(ROTATE_BYTES // self.wbytes) + 1)
-        self.copies = [base] + [(base[0].clone(), base[1].clone()) for _ in range(ncopy - 1)]
+        self.bufs, self.copies = [], []
+        for _ in range(ncopy):
+            buf, views, _ = packed_copy(torch, base)
+            self.bufs.append(buf)
+            self.copies.append(tuple(views))
+        del base
         self.y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
         self.bytes = self.wbytes + M * K * 2 + M * N * 2
         self.flops = 2.0 * M * N * K
@@ -263,6 +356,23 @@ class Decode:
         wq, sc = self.copies[i % len(self.copies)]
         wdt, sdt, grp = self.meta
         self.W.wq_gemm(self.x, wq, wdt, sc, sdt, grp, self.N, y=self.y, alpha=self.alpha)
+
+    def stream(self, i):
+        """Read-only stream of copy i's weights and scales (the footprint the
+        GEMV must read from HBM, x and y aside)."""
+        self.W.wq_util_stream_read(self.bufs[i % len(self.bufs)])
+
+
+class BigStream:
+    """Read-only stream of a 2 GiB buffer (the steady-state HBM read rate)."""
+
+    def __init__(self, torch, W, nbytes=2 << 30):
+        self.W = W
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+        self.bytes = nbytes
+
+    def launch(self, i):
+        self.W.wq_util_stream_read(self.buf)
 
 
 class Prefill:
@@ -499,14 +609,16 @@ def main():
               "quant_mxfp4": lambda: ActQuant(torch, W, "mxfp4"), "copy": lambda: Copy(torch),
               "quant_mxfp8": lambda: ActQuant(torch, W, "mxfp8"),
               "wquant_mxfp4": lambda: WeightQuant(torch, W),
-              "moe_gate_up": lambda: MoeW4A8(torch, W, "gate_up"), "moe_down": lambda: MoeW4A8(torch, W, "down")}[case]
+              "moe_gate_up": lambda: MoeW4A8(torch, W, "gate_up"), "moe_down": lambda: MoeW4A8(torch, W, "down"),
+              "stream_decode": lambda: Decode(torch, W, 1), "stream_2g": lambda: BigStream(torch, W)}[case]
         obj = mk()
         big = case in ("prefill", "prefill_nvfp4", "moe_gate_up", "moe_down", "w8a8_block", "w8a8_channel")
         reps = args.reps or (20 if big else 100)
         # the clocks settle over the first launches of a large kernel: the
         # profile's median then reflects the steady state, as the timed runs do
+        fn = obj.stream if case == "stream_decode" else obj.launch
         for i in range(reps + (3 if big else 0)):
-            obj.launch(i)
+            fn(i)
         torch.cuda.synchronize()
         print(f"{case}: {reps} launches done", flush=True)
         return
@@ -516,31 +628,44 @@ def main():
     timed_g = graph_of(torch, [lambda i=i: dec.launch(i) for i in range(K)])
     warm_g.replay()
     torch.cuda.synchronize()
+    region = Region(torch, W, timed_g.replay, K, rounds=args.rounds)
     clocks = ClockSampler(torch)
     t0 = time.perf_counter()
     with clocks:
-        ms = time_graph(torch, timed_g, K)
+        ms = region.run()
     wall = time.perf_counter() - t0
-    clock_summary = {"decode_timed_region": clocks.summary()}
+    clock_summary = {"decode_timed_regions": clocks.summary(),
+                     "decode_per_region": clocks.per_window(region.windows)}
     value = dec.bytes / (ms * 1e-3) / 1e9
+    # the measured denominator: a read-only stream of the same weight copies,
+    # same rotation, same timing method
+    stream_g = graph_of(torch, [lambda i=i: dec.stream(i) for i in range(K)])
+    stream_g.replay()
+    sreg = Region(torch, W, stream_g.replay, K, rounds=args.rounds)
+    ms_s = sreg.run()
+    stream_gbs = dec.wbytes / (ms_s * 1e-3) / 1e9
     traffic = stored_traffic("decode_w4a16_m1", dec.bytes)
     roofline = {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(value / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "k_gemv_ring<INT4> (wq_gemm, M<=4 decode path)",
-                "bytes_per_launch": dec.bytes, "us_per_launch": round(ms * 1e3, 3)}
-    del timed_g, warm_g
+                "kernel": DECODE_KERNEL, "bytes_per_launch": dec.bytes, "us_per_launch": round(ms * 1e3, 3),
+                "timing": region.describe(),
+                "stream_read_same_footprint": {"bytes": dec.wbytes, "us": round(ms_s * 1e3, 3),
+                                               "GB/s": round(stream_gbs, 1), "timing": sreg.describe()},
+                "frac_of_stream_read": round(ms_s / ms, 4)}
+    del timed_g, warm_g, stream_g
     if args.only == "decode":
         print(json.dumps({"case": "decode", "us_per_launch": roofline["us_per_launch"], "GB/s": roofline["achieved"],
-                          "launches_timed": K, "warmup": Wm}), flush=True)
+                          "launches_timed": K, "warmup": Wm, "timing": region.describe(),
+                          "stream_read_us": roofline["stream_read_same_footprint"]["us"]}), flush=True)
         return
 
     secondary = {}
 
     def add_decode(label, M, kind):
         d = Decode(torch, W, M, kind)
-        g = graph_of(torch, [lambda i=i: d.launch(i) for i in range(100)])
+        g = graph_of(torch, [lambda i=i: d.launch(i) for i in range(50)])
         g.replay()
-        t = time_graph(torch, g, 100)
+        t = Region(torch, W, g.replay, 50, rounds=3).run()
         secondary[label] = {"GB/s": round(d.bytes / (t * 1e-3) / 1e9, 1), "us": round(t * 1e3, 3),
                             "frac_hbm": round(d.bytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bytes": d.bytes}
         del g, d
@@ -561,10 +686,19 @@ def main():
     secondary["prefill_mxfp4_m8192"] = {"TFLOP/s": round(tf, 1), "frac_bf16_mfma": round(tf / BF16_PEAK_TFLOPS, 4),
                                         "ms": round(t, 3), "flops": pf.flops}
     # secondary denominator: torch.matmul bf16 (hipBLASLt) at the same shape
-    wb = torch.empty((pf.N, pf.K), dtype=torch.bfloat16, device="cuda").normal_()
-    t2 = time_eager(torch, lambda i: torch.matmul(pf.x, wb.t()), 10)
+    # on the same values (the dequantized MXFP4 weights), timed in rounds
+    # interleaved with the kernel's
+    wb = W.wq_dequant(pf.codes, W.WQ_E2M1X2, pf.sc, W.WQ_E8M0, 32, pf.N, pf.K)
+    tk, tt = [], []
+    for _ in range(3):
+        tk.append(time_eager(torch, pf.launch, 10, warm=1, rounds=1))
+        tt.append(time_eager(torch, lambda i: torch.matmul(pf.x, wb.t()), 10, warm=1, rounds=1))
+    t2 = float(np.median(tt))
     secondary["torch_matmul_bf16_8192x14336x4096"] = {"TFLOP/s": round(pf.flops / (t2 * 1e-3) / 1e12, 1),
-                                                      "ms": round(t2, 3)}
+                                                      "ms": round(t2, 3), "weights": "the dequantized MXFP4 weights"}
+    secondary["prefill_mxfp4_vs_torch_interleaved"] = {"kernel_ms": [round(v, 3) for v in tk],
+                                                      "torch_ms": [round(v, 3) for v in tt],
+                                                      "ratio_of_medians": round(float(np.median(tk)) / t2, 4)}
     del pf, wb
     pf = Prefill(torch, W, kind="nvfp4")
     t = time_eager(torch, pf.launch, 10)
@@ -622,6 +756,10 @@ def main():
     t = time_eager(torch, cp.launch, 20)
     secondary["stream_copy_256MiB"] = {"GB/s": round(cp.bytes / (t * 1e-3) / 1e9, 1)}
     del cp
+    bs = BigStream(torch, W)
+    t = time_eager(torch, bs.launch, 10)
+    secondary["stream_read_2GiB"] = {"GB/s": round(bs.bytes / (t * 1e-3) / 1e9, 1), "us": round(t * 1e3, 1)}
+    del bs
     torch.cuda.empty_cache()
 
     cpu = None if args.no_cpu else cpu_baseline()

@@ -1,20 +1,24 @@
-"""The C-ABI library loads and exports every entry point include/wq.h declares;
-invalid arguments are rejected on the host before any launch (CPU only)."""
+"""The C-ABI library loads and exports every entry point the headers under
+include/ declare; invalid arguments are rejected on the host before any launch
+(CPU only)."""
 import ctypes
+import glob
 import os
 import re
 
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "wq.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 LIB = os.path.join(ROOT, "weight_only_quantized_quant_amd", "libwq.so")
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -29,7 +33,7 @@ def test_header_declares_the_entry_points():
     for n in ("quantize_e4m3", "quantize_mxfp4", "quantize_mx", "quantize_nvfp4", "quantize_int4", "quantize_int4_asym", "wq_dequant", "wq_gemm",
               "wq_gemm_workspace_size", "wq_status_string", "wq_moe_route", "wq_w4a8_prepack",
               "wq_w4a8_dequant", "wq_moe_gemm_w4a8", "quantize_e4m3_static", "quantize_e4m3_block2d",
-              "wq_gemm_w8a8"):
+              "wq_gemm_w8a8", "wq_util_stream_read", "wq_util_spin"):
         assert n in names
 
 
@@ -180,3 +184,21 @@ def test_moe_invalid_arguments_rejected_before_launch(lib):
     assert gm(*args(16, 32, 128, rt=None)) == 1                          # identity rows need R == T
     assert gm(*args(16, 32, 128, x=q)) == 2
     assert gm(*args(0, 0, 128)) == 1
+
+
+def test_utilities_reject_bad_arguments(lib):
+    sr = lib.wq_util_stream_read
+    sr.restype = ctypes.c_int
+    sr.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]
+    fake = 1 << 20                                       # never dereferenced: rejected on the host
+    assert sr(None, 1024, 0, fake, None) == 1
+    assert sr(fake, 0, 0, fake, None) == 1
+    assert sr(fake, 1000, 0, fake, None) == 1            # not a multiple of 16
+    assert sr(fake, 1024, 0, None, None) == 1
+    assert sr(fake + 8, 1024, 0, fake, None) == 2        # misaligned
+    sp = lib.wq_util_spin
+    sp.restype = ctypes.c_int
+    sp.argtypes = [ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]
+    assert sp(0, 0, fake, None) == 1
+    assert sp((1 << 24) + 1, 0, fake, None) == 1
+    assert sp(100, 0, None, None) == 1

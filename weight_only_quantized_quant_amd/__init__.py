@@ -27,7 +27,7 @@ MX_ELEMS = {"e2m1": WQ_E2M1X2, "e4m3": WQ_E4M3}
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m weight_only_quantized_quant_amd.build` "
+        f"{LIB_PATH} is missing: build it with `python weight_only_quantized_quant_amd/build.py` "
         "(hipcc, gfx950). There is no fallback path.")
 
 lib = ctypes.CDLL(LIB_PATH)
@@ -52,6 +52,8 @@ _SIGS = {
     "wq_w4a8_prepack": ([_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp], ctypes.c_int),
     "wq_w4a8_dequant": ([_vp, _vp, _i64, _i64, _vp, _vp], ctypes.c_int),
     "wq_moe_gemm_w4a8": ([_vp, _i64, _vp, _vp, _i64, _vp, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "wq_util_stream_read": ([_vp, _i64, ctypes.c_uint32, _vp, _vp], ctypes.c_int),
+    "wq_util_spin": ([_i64, ctypes.c_uint32, _vp, _vp], ctypes.c_int),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -387,3 +389,35 @@ def wq_moe_gemm_w4a8(x8: torch.Tensor, a_scale: torch.Tensor, row_token, offsets
                                 wq.data_ptr(), s8.data_ptr(), ch.data_ptr(), y.data_ptr(), _stream()),
            "wq_moe_gemm_w4a8")
     return y
+
+
+# ---------------------------------------------------------------------------
+# measurement utilities (include/wq_util.h)
+# ---------------------------------------------------------------------------
+_SINK = {}
+_MAGIC = 0x9E3779B9
+
+
+def _sink(device) -> torch.Tensor:
+    key = str(device)
+    if key not in _SINK:
+        _SINK[key] = torch.zeros(4, dtype=torch.int32, device=device)
+    return _SINK[key]
+
+
+def wq_util_stream_read(buf: torch.Tensor, nbytes: int = None) -> None:
+    """Read the first `nbytes` bytes of `buf` (all of it by default) once from
+    device memory and discard them."""
+    _dev(buf, "buf")
+    total = buf.numel() * buf.element_size()
+    nbytes = total if nbytes is None else int(nbytes)
+    if nbytes > total:
+        raise ValueError("nbytes exceeds the buffer")
+    _check(lib.wq_util_stream_read(buf.data_ptr(), nbytes, _MAGIC, _sink(buf.device).data_ptr(), _stream()),
+           "wq_util_stream_read")
+
+
+def wq_util_spin(iters: int, device=None) -> None:
+    """Enqueue a bounded busy kernel of `iters` iterations (one workgroup per CU)."""
+    dev = torch.device("cuda") if device is None else torch.device(device)
+    _check(lib.wq_util_spin(int(iters), _MAGIC, _sink(dev).data_ptr(), _stream()), "wq_util_spin")
