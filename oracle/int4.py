@@ -8,10 +8,18 @@ roofline") group size 128 along K with a 16-bit scale per group.
 
 Readings where the pages are silent:
 * qmax = 7 (the largest positive code), so a symmetric group never needs -8;
-* the scale is rounded once more, to bf16 (round to nearest even), and the
-  group is quantized with that stored scale, so that dequantization is
-  self-consistent: s = bf16(RN_f32(amax / 7)); a scale that is zero after
-  either rounding (including the all-zero group) is replaced by 1;
+* the scale is stored as a bf16 value whose significand has at most 5
+  significant bits: s = RN_5(RN_f32(amax / 7)), the fp32 quotient rounded to
+  the nearest multiple of 2^(e-4) (e its binary exponent; 2^-130 below the
+  normal range), ties to even.  The pages fix the scale as amax / qmax and the
+  dequantized weight as (q - z) * s cast to the element type, but not the
+  precision of the stored scale; with a 5-bit significand every product q * s
+  (|q| <= 8) has at most 8 significant bits, so the cast to bf16 is exact and
+  the dequantized weight equals q * s.  The group is quantized with the stored
+  scale, so that dequantization is self-consistent; a scale that is zero
+  after the rounding (including the all-zero group) is replaced by 1.  The
+  rounding moves the scale by at most 2^-5 of itself, so amax / s stays in
+  [6.79, 7.23] and the largest element of a group always gets |q| = 7;
 * q = clamp(rint(RN_f32(x / s)), -8, 7): an IEEE fp32 division, then round
   half to even;
 * packing: eight two's-complement nibbles per uint32, element 8i + j in bits
@@ -26,9 +34,19 @@ import numpy as np
 from .formats import bf16_decode, bf16_round
 
 
+def round_significand5(v) -> np.ndarray:
+    """Nearest value with a 5-bit significand (multiples of 2^(e-4) in the
+    binade [2^e, 2^(e+1)), of 2^-130 below 2^-126), ties to even; fp64 in and
+    out (every such value and every fp32 input is exact in fp64)."""
+    v = np.asarray(v, dtype=np.float64)
+    _, ex = np.frexp(v)                                                   # v = m 2^ex, m in [0.5, 1)
+    ulp = np.maximum(np.ldexp(1.0, ex - 5), 2.0 ** -130)
+    return np.rint(v / ulp) * ulp                                         # v / ulp exact: power-of-two ulp
+
+
 def int4_scale_bits(amax_f32) -> np.ndarray:
     s32 = np.asarray(amax_f32, dtype=np.float32) / np.float32(7.0)       # IEEE fp32
-    bits = bf16_round(s32.astype(np.float64))
+    bits = bf16_round(round_significand5(s32.astype(np.float64)))        # exact: 5 significant bits
     return np.where(bf16_decode(bits) == 0, np.uint16(0x3F80), bits).astype(np.uint16)
 
 

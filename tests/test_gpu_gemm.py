@@ -109,6 +109,30 @@ def test_gemv_int4_small_groups_long_k(W, group, M):
     _check(W.wq_gemm(dev_bf16(xbits), *args, N), xbits, wdeq, chan)
 
 
+@pytest.mark.parametrize("form", ["short", "long", "mixed"])
+@pytest.mark.parametrize("M,N,K", [(1, 14336, 4096), (3, 4795, 4096), (4, 4105, 1024), (1, 300, 512)])
+def test_gemv_int4_scale_forms(W, form, M, N, K):
+    # The quantizer stores scales with a 5-bit significand, for which the decode
+    # multiplies the codes exactly and scales the group sums; any other bf16
+    # scale in a step sends that step through the per-weight conversion.
+    # "long": every scale gets nonzero low mantissa bits; "mixed": one group
+    # in ten does, so waves switch between the two forms step by step.
+    g = np.random.default_rng(M * 31 + N + K)
+    Wf = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
+    Wf[g.choice(N, 7, replace=False)] *= 25
+    xbits = to_bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    packed, sb, _ = OI.quantize_int4(Wf, 128)
+    assert np.all(sb & 7 == 0)
+    if form != "short":
+        low = g.integers(1, 8, sb.shape).astype(np.uint16)
+        if form == "mixed":
+            low = np.where(g.random(sb.shape) < 0.1, low, 0).astype(np.uint16)
+        sb = (sb | low).astype(np.uint16)
+    banner("gemv int4 scales", form, M, N, K)
+    y = W.wq_gemm(dev_bf16(xbits), dev_words(packed), W.WQ_INT4X8, dev_bf16(sb), W.WQ_BF16, 128, N)
+    _check(y, xbits, OD.dequant_int4(packed, sb, 128), None)
+
+
 def test_gemv_mxfp4_small_config(W):
     xbits, Wf = mxfp4_gemv_inputs(0)
     args, wdeq, chan = _prep(W, "mxfp4", Wf)

@@ -29,6 +29,35 @@ def test_int4_range_and_overhead():
     assert q.min() >= -8 and q.max() <= 7
 
 
+_SHORT_BF16 = np.arange(8, 0x7F80, 8, dtype=np.uint32).astype(np.uint16)      # low 3 mantissa bits zero
+
+
+def _nearest_short_bf16(v):
+    """Brute force: the positive bf16 value with 3 trailing zero mantissa bits
+    nearest to each v (fp64), ties to the one whose bit 3 is clear."""
+    cand = bf16_decode(_SHORT_BF16).astype(np.float64)
+    i = np.clip(np.searchsorted(cand, v), 1, len(cand) - 1)
+    lo, hi = cand[i - 1], cand[i]
+    pick_hi = (hi - v < v - lo) | ((hi - v == v - lo) & ((_SHORT_BF16[i] & 8) == 0))
+    return np.where(pick_hi, _SHORT_BF16[i], _SHORT_BF16[i - 1])
+
+
+def test_int4_scale_makes_every_product_exact_in_bf16():
+    # every stored scale has 3 trailing zero mantissa bits, and then q * s is a
+    # bf16 value for every code: dequantization involves no rounding
+    g = np.random.default_rng(3)
+    w = (g.standard_normal((16, 1024)) * np.exp2(g.integers(-40, 40, (16, 1)))).astype(np.float32)
+    _, sb, _ = I4.quantize_int4(w, 128)
+    assert np.all(sb & 7 == 0)
+    s = bf16_decode(sb).astype(np.float64)
+    prods = s[..., None] * np.arange(-8, 8)
+    assert np.array_equal(bf16_decode(bf16_round(prods)), prods)
+    # a 6-bit significand would not have this property (negative control)
+    s6 = bf16_decode(sb | 4).astype(np.float64)
+    p6 = s6[..., None] * np.arange(-8, 8)
+    assert not np.array_equal(bf16_decode(bf16_round(p6)), p6)
+
+
 def test_int4_bruteforce_and_bound():
     g = np.random.default_rng(1)
     w = (g.standard_normal((8, 256)) * np.exp2(g.integers(-10, 10, (8, 1)))).astype(np.float32)
@@ -48,9 +77,16 @@ def test_int4_bruteforce_and_bound():
         unclamped = np.abs(r) <= 7.5
         bound = np.broadcast_to(s[:, :, None].astype(np.float64) * 0.5 * (1 + 2.0 ** -20), r.shape)
         assert np.all(err[unclamped] <= bound[unclamped])
-        # scale is bf16(RN_f32(amax/7)), rounded by torch's cast as an independent check
+        # the scale is the bf16 value with a 5-bit significand nearest to
+        # RN_f32(amax/7), ties to the even significand, found here by a search
+        # over every such positive bf16 value
         amax = np.abs(w.reshape(r.shape)).max(axis=2)
-        assert np.array_equal(sb, _torch_bf16_bits((amax / np.float32(7)).astype(np.float32)))
+        v = (amax / np.float32(7)).astype(np.float32).astype(np.float64).ravel()
+        assert np.array_equal(sb.ravel(), _nearest_short_bf16(v))
+        # the largest element of every group gets |q| = 7
+        qg = np.abs(q.reshape(r.shape).astype(np.int64))
+        at_max = np.abs(w.reshape(r.shape)) == amax[:, :, None]
+        assert np.all(qg[at_max] == 7)
 
 
 def test_int4_zero_group_and_pack():

@@ -115,6 +115,32 @@ __device__ __forceinline__ void dq_int4_word(uint32_t w, float s, uint32_t out[4
   dq_u4_bytes(ue, uo, s, s * -8.0f, out);
 }
 
+// INT4 word -> bf16 patterns of q + 136 for its 8 codes: 136 + q = 128 + u with
+// u = q + 8 the offset-binary code, and bf16(128 + u) = 0x4300 | u exactly, so
+// no conversion is needed.  out[i] holds elements 2i (low half) and 2i + 1
+// (high half), the element order of dq_int4_word.  v_perm places byte i of w
+// (elements 2i and 2i + 1 in its low and high nibble) in byte 0 and byte i of
+// w >> 4 (element 2i + 1 in its low nibble) in byte 2; one v_bitop3 keeps the
+// two low nibbles, flips their top bit (u = nibble ^ 8) and sets 0x4300.
+__device__ __forceinline__ void dq_int4_word_o136(uint32_t w, uint32_t out[4]) {
+  constexpr uint8_t AND_XOR = (uint8_t)((0xF0 & 0xCC) ^ 0xAA);
+  const uint32_t w4 = w >> 4;
+  out[0] = __builtin_amdgcn_bitop3_b32(__builtin_amdgcn_perm(w4, w, 0x00040000u), 0x000F000Fu, 0x43084308u, AND_XOR);
+  out[1] = __builtin_amdgcn_bitop3_b32(__builtin_amdgcn_perm(w4, w, 0x00050001u), 0x000F000Fu, 0x43084308u, AND_XOR);
+  out[2] = __builtin_amdgcn_bitop3_b32(__builtin_amdgcn_perm(w4, w, 0x00060002u), 0x000F000Fu, 0x43084308u, AND_XOR);
+  out[3] = __builtin_amdgcn_bitop3_b32(__builtin_amdgcn_perm(w4, w, 0x00070003u), 0x000F000Fu, 0x43084308u, AND_XOR);
+}
+// bf16 patterns of -136 (two per word), the offset's correction operand.
+constexpr uint32_t kBf16Neg136x2 = 0xC308C308u;
+
+// A bf16 INT4 scale whose significand has at most 5 significant bits (3
+// trailing zero mantissa bits) and whose magnitude is below 2^124: every
+// product q * s with q in [-8, 7] is then a finite bf16 value, computed
+// exactly, so bf16(q * s) = q * s.
+__device__ __forceinline__ bool int4_scale_short(uint32_t bits16) {
+  return (bits16 & 7u) == 0u && (bits16 & 0x7F80u) <= 0x7D00u;
+}
+
 // Unsigned INT4 word (8 codes q in [0, 15]) with scale s and bias b = -z * s:
 // fma(q, s, b) = (q - z) * s exactly (both products have at most 12
 // significant bits for a bf16 s and z <= 15), then one RNE conversion per

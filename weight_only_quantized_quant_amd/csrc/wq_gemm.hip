@@ -14,6 +14,8 @@
 // v_mfma_f32_32x32x16_bf16.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "wq.h"
 #include "wq_device.h"
 #include "wq_host.h"
@@ -899,42 +901,84 @@ __device__ __forceinline__ void gemv_ring_tile(const uint16_t* __restrict__ x, i
   const int tok = HALF ? (nl & 7) : nl;                       // token of this lane's x operand row
   const int xtr = tok < M ? tok : 0;
   const uint8_t* xrow = XS ? ring + 1024 + hp * XCH + xtr * XRB : xl + (hp * M + xtr) * XROW;
+  // FASTQ: the INT4 form without per-weight conversion (see below), chosen
+  // once per wave for all of its steps
+  auto run_steps = [&](auto fast_tag) {
+    constexpr bool FASTQ = decltype(fast_tag)::value;
 #pragma unroll
-  for (int c = 0; c < SPWE; c++) {
-    // step loads issued after step c's: min(R-1, SPWE-1-c) steps of VMS loads
-    // (each step issues its refill after this wait)
-    wait_vm_n(REGW ? SPWE - 1 - c : (c + R - 1 < SPWE ? R - 1 : SPWE - 1 - c) * VMS);
-    if (!REGW && c + R < SPWE) {
-      // step c + R goes to the slot step c - 1 read: that read returned before
-      // step c - 1's conversion, and nothing may be scheduled across the
-      // barrier (a DMA write is not ordered after an earlier LDS read)
-      __builtin_amdgcn_sched_barrier(0);
-      issue_step((c + R) % NS, c + R);
+    for (int c = 0; c < SPWE; c++) {
+      // step loads issued after step c's: min(R-1, SPWE-1-c) steps of VMS loads
+      // (each step issues its refill after this wait)
+      wait_vm_n(REGW ? SPWE - 1 - c : (c + R - 1 < SPWE ? R - 1 : SPWE - 1 - c) * VMS);
+      if (!REGW && c + R < SPWE) {
+        // step c + R goes to the slot step c - 1 read: that read returned before
+        // step c - 1's conversion, and nothing may be scheduled across the
+        // barrier (a DMA write is not ordered after an earlier LDS read)
+        __builtin_amdgcn_sched_barrier(0);
+        issue_step((c + R) % NS, c + R);
+      }
+      const u32x4_t wv = REGW ? wreg[c] : *reinterpret_cast<const u32x4_t*>(ring + (c % NS) * SLOT + lane * 16);
+      scale_t<WDT> scv{};
+      if constexpr (WDT == W_INT4) {
+        const uint32_t gi = (uint32_t)(c * KSTEP + EPL * g) >> gs;
+        scv = bf16_to_f32(sdma ? (uint32_t)*reinterpret_cast<const uint16_t*>(sl + nl * srs + 2 * gi) : svr[c]);
+      } else if constexpr (WDT == W_FP4) {
+        const uint32_t gi = (uint32_t)(c * KSTEP + EPL * g) >> 5;
+        scv = sdma ? e8m0_as_scale(sl[nl * srs + gi]) : scale_from_raw<WDT>(svr[c]);
+      } else if constexpr (WDT == W_NV4) {
+        const uint32_t gi = (uint32_t)(c * KSTEP + EPL * g) >> 4;
+        scv = scale_from_raw<WDT>(sdma ? (uint32_t)*reinterpret_cast<const uint16_t*>(sl + nl * srs + gi) : svr[c]);
+      } else if constexpr (WDT == W_UINT4) {
+        const uint32_t gi = (uint32_t)(c * KSTEP + EPL * g) >> gs;
+        scv = scale_from_raw<WDT>(sdma ? *reinterpret_cast<const uint32_t*>(sl + nl * srs + 4 * gi) : svr[c]);
+      }
+      bf16x8_t xa[MF];
+#pragma unroll
+      for (int j = 0; j < MF; j++)
+        xa[j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(
+            xrow + (XS ? (c % NS) * SLOT + (EPL * g + 8 * j) * 2 : (c * KSTEP + EPL * g + 8 * j) * 2)));
+      if constexpr (FASTQ) {
+        if constexpr (WDT == W_INT4) {
+          const bf16x8_t neg136 = as_bf16x8(kBf16Neg136x2, kBf16Neg136x2, kBf16Neg136x2, kBf16Neg136x2);
+          f32x4_t pq = f32x4_t{0.f, 0.f, 0.f, 0.f}, pc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int j = 0; j < MF; j++) {
+            uint32_t o[4];
+            dq_int4_word_o136(wv[j], o);
+            pq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[j], as_bf16x8(o[0], o[1], o[2], o[3]), pq, 0, 0, 0);
+            pc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[j], neg136, pc, 0, 0, 0);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; i++) acc[i] = __builtin_fmaf(scv, pq[i] + pc[i], acc[i]);
+        }
+      } else {
+        bf16x8_t b[4];
+        dequant16<WDT>(wv, scv, b);
+#pragma unroll
+        for (int j = 0; j < MF; j++) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[j], b[j], acc, 0, 0, 0);
+      }
     }
-    const u32x4_t wv = REGW ? wreg[c] : *reinterpret_cast<const u32x4_t*>(ring + (c % NS) * SLOT + lane * 16);
-    scale_t<WDT> scv{};
-    if constexpr (WDT == W_INT4) {
-      const uint32_t gi = (uint32_t)(c * KSTEP + EPL * g) >> gs;
-      scv = sdma ? bf16_to_f32(*reinterpret_cast<const uint16_t*>(sl + nl * srs + 2 * gi)) : scale_from_raw<WDT>(svr[c]);
-    } else if constexpr (WDT == W_FP4) {
-      const uint32_t gi = (uint32_t)(c * KSTEP + EPL * g) >> 5;
-      scv = sdma ? e8m0_as_scale(sl[nl * srs + gi]) : scale_from_raw<WDT>(svr[c]);
-    } else if constexpr (WDT == W_NV4) {
-      const uint32_t gi = (uint32_t)(c * KSTEP + EPL * g) >> 4;
-      scv = scale_from_raw<WDT>(sdma ? (uint32_t)*reinterpret_cast<const uint16_t*>(sl + nl * srs + gi) : svr[c]);
-    } else if constexpr (WDT == W_UINT4) {
-      const uint32_t gi = (uint32_t)(c * KSTEP + EPL * g) >> gs;
-      scv = scale_from_raw<WDT>(sdma ? *reinterpret_cast<const uint32_t*>(sl + nl * srs + 4 * gi) : svr[c]);
-    }
-    bf16x8_t xa[MF];
+  };
+  // INT4 groups of 128: a step covers one group per row.  When every scale of
+  // the wave's slice has a 5-bit significand, bf16(q * s) = q * s, so
+  // x . bf16(q s) = s * (x . (q + 136) + x . (-136)): the codes go to the MFMA
+  // as the exact bf16 patterns of q + 136 (no conversion), a second MFMA chain
+  // against the constant -136 removes the offset, and the fp32 group sum is
+  // scaled once.  The two chains take the same x fragments in the same order
+  // into separate accumulators, so for all-zero codes they are exact negatives
+  // of each other and the group adds exactly zero.  Otherwise every weight is
+  // converted to bf16(q s).  The choice waits for the first step's loads (the
+  // scales were issued before them), as the first step would.
+  if constexpr (WDT == W_INT4 && gs == 7) {
+    wait_vm_n(REGW ? SPWE - 1 : (R - 1 < SPWE ? R - 1 : SPWE - 1) * VMS);
+    bool mine = true;
 #pragma unroll
-    for (int j = 0; j < MF; j++)
-      xa[j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(
-          xrow + (XS ? (c % NS) * SLOT + (EPL * g + 8 * j) * 2 : (c * KSTEP + EPL * g + 8 * j) * 2)));
-    bf16x8_t b[4];
-    dequant16<WDT>(wv, scv, b);
-#pragma unroll
-    for (int j = 0; j < MF; j++) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[j], b[j], acc, 0, 0, 0);
+    for (int c = 0; c < SPWE; c++)
+      mine &= int4_scale_short(sdma ? (uint32_t)*reinterpret_cast<const uint16_t*>(sl + nl * srs + 2 * c) : svr[c]);
+    if (__builtin_amdgcn_ballot_w64(!mine) == 0) run_steps(std::true_type{});
+    else run_steps(std::false_type{});
+  } else {
+    run_steps(std::false_type{});
   }
 
   // split-K reduction in the (consumed) front of the workgroup's LDS

@@ -290,7 +290,12 @@ __global__ __launch_bounds__(kThreads) void k_int4(const void* __restrict__ x, i
   load8<BF16>(x, t * 16 + 8, v + 8);
   float m = __builtin_fmaxf(absmax8(v), absmax8(v + 8));
   m = group_max(m, lanes_per_group);
-  uint32_t sb = f32_to_bf16_bits(m / 7.0f);   // bf16(RN_f32(amax / 7))
+  // RN_f32(amax / 7) rounded to a 5-bit significand, ties to even: the fp32
+  // pattern rounded at mantissa bit 19 (a carry moves into the exponent), which
+  // is a bf16 value with 3 trailing zero mantissa bits, so that q * s is exact
+  // in bf16 for every code
+  const uint32_t qb = __float_as_uint(m / 7.0f);
+  uint32_t sb = ((qb + 0x3FFFFu + ((qb >> 19) & 1u)) & 0xFFF80000u) >> 16;
   if ((sb & 0x7FFFu) == 0u) sb = 0x3F80u;
   const float s = bf16_to_f32(sb);
   uint32_t w[2] = {0u, 0u};
