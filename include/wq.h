@@ -254,7 +254,11 @@ wq_status wq_dequant(const void* wq, int w_dtype, const void* w_scales, int s_dt
  * sections 2 and 4.1 (bf16 x bf16 multiply after in-register dequantization).
  *
  * Weight/scale pairs:
- *   WQ_INT4X8 + WQ_BF16  group in {32, 64, 128}; scales in (0, 2^120]
+ *   WQ_INT4X8 + WQ_BF16  group in {32, 64, 128}; scales in (0, 2^120].  With
+ *                         group 128, decode steps whose scales all have 3
+ *                         trailing zero mantissa bits (what quantize_int4
+ *                         writes) multiply the exact codes and scale the
+ *                         group sums; the result is the same product.
  *   WQ_UINT4X8 + WQ_BF16Z  group in {32, 64, 128} (asymmetric INT4, operand
  *                         bf16((q - z) * s)); scales in (0, 2^120], z <= 15
  *   WQ_E2M1X2 + WQ_E8M0  group 32 (MXFP4)
@@ -266,7 +270,10 @@ wq_status wq_dequant(const void* wq, int w_dtype, const void* w_scales, int s_dt
  *         per-tensor scale of NVFP4; 1 otherwise).  Non-finite: WQ_EINVAL.
  *         y = bf16(acc * RN(chan * alpha)) for WQ_E4M3 weights,
  *         y = bf16(acc * alpha) for the others.
- * M >= 1, N >= 1, K % 128 == 0.  M <= 32 runs the split-K decode kernels;
+ * M >= 1, N >= 1, K % 128 == 0 for every weight format, including INT4
+ * groups of 32 or 64 and MXFP4 blocks of 32 (the kernels step K in 128-element
+ * chunks of one 16-byte load per lane and have no tail path; a K that is only
+ * a multiple of the group returns WQ_EINVAL).  M <= 32 runs the split-K decode kernels;
  * 32 < M <= 64 runs them twice, on rows 0-31 and on the rest (both launches
  * on `stream`); larger M the MFMA prefill kernel, except that for
  * 64 < M <= 256 the decode launches (one per 32 rows) are taken when a cost
@@ -417,7 +424,13 @@ wq_status wq_w4a8_dequant(const uint32_t* wq, const uint8_t* s8, int64_t N, int6
  * x8        T x K E4M3 codes (per-token quantized activations), a_scale T fp32
  *           (quantize_e4m3 with block -1 produces both).  T*K < 2^31.
  * row_token R int32 or NULL; offsets experts + 1 int32 (device), offsets[0] = 0,
- *           non-decreasing, offsets[experts] = R.
+ *           non-decreasing, offsets[experts] = R (wq_moe_route writes such
+ *           arrays).  Both are device data the host cannot check; the kernel
+ *           clamps every expert's row range to [0, R] (a decreasing or
+ *           out-of-range pair of offsets gives an empty expert) and treats a
+ *           row_token entry outside [0, T) as a zero row with scale 0, so no
+ *           access leaves the buffers, but the rows of such an expert are then
+ *           not computed as the formula above states.
  * wq, s8, ch  from wq_w4a8_prepack, experts x N x ...; K % 128 == 0.
  * y         R x N bf16 (output), rows in grouped order.
  * The fp8 MFMA treats E4M3 subnormal operands as zero; results differ from the

@@ -100,6 +100,11 @@ def test_invalid_arguments_rejected_before_launch(lib):
     args = lambda M, N, K, wdt, sdt, grp, x=p, a=1.0: (x, _i64(M), _i64(N), _i64(K), p, wdt, p, sdt, grp,
                                                       ctypes.c_float(a), p, None, ctypes.c_size_t(0), None)
     assert gm(*args(1, 16, 100, 5, 1, 128)) == 1                        # K % 128
+    # K a multiple of the group but not of 128: rejected for every format
+    assert gm(*args(1, 16, 96, 5, 1, 32)) == 1                          # INT4 group 32
+    assert gm(*args(4, 16, 192, 5, 1, 64)) == 1                         # INT4 group 64
+    assert gm(*args(1, 16, 160, 3, 4, 32)) == 1                         # MXFP4 block 32
+    assert gm(*args(300, 16, 224, 6, 7, 32)) == 1                       # asymmetric INT4, prefill rows
     assert gm(*args(0, 16, 128, 5, 1, 128)) == 1
     assert gm(*args(1, 16, 128, 5, 1, 96)) == 3                         # bad group
     assert gm(*args(1, 16, 128, 3, 1, 32)) == 3                         # fp4 needs E8M0

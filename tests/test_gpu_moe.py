@@ -198,6 +198,43 @@ def test_moe_gemm_small(W, T, E, k, K, N):
     _small_case(W, T, E, k, K, N, seed=T + E + k + K + N)
 
 
+def test_moe_gemm_clamps_device_offsets_and_tokens(W):
+    # offsets and row_token are device data the host cannot validate: the
+    # kernel clamps every expert's rows to [0, R] and reads a token index
+    # outside [0, T) as a zero row.  A run with offsets[E] far past R and a
+    # few bad token indices must match the well-formed run on every other row
+    # and give zeros on the rows with bad tokens.
+    g = np.random.default_rng(77)
+    T, E, k, K, N = 200, 4, 2, 256, 96
+    ids, _ = OW.route_topk(g.standard_normal((T, E)).astype(np.float32), k)
+    offsets, row_token, _ = OW.group_by_expert(ids, E)
+    R = T * k
+    xbits = to_bf16_bits(g.standard_normal((T, K)).astype(np.float32))
+    x8, a_s = OW.quantize_tokens(xbits)
+    packed, sbits = [], []
+    for e in range(E):
+        p, sb, _ = OI.quantize_int4((g.standard_normal((N, K)) * 0.02).astype(np.float32), 128)
+        packed.append(p)
+        sbits.append(sb)
+    wq2, s8d, chd = W.wq_w4a8_prepack(dev_words(np.stack(packed)), dev_bf16(np.stack(sbits)))
+    bad_rows = np.array([0, 17, R - 1])
+    rt_bad = row_token.astype(np.int32).copy()
+    rt_bad[bad_rows] = [-5, T + 7, 2 ** 30]
+    off_bad = offsets.astype(np.int32).copy()
+    off_bad[E] = R + 100000
+    banner("moe gemm clamps offsets and token indices")
+    args = (dev_u8(x8), dev_f32(a_s))
+    y_ok = W.wq_moe_gemm_w4a8(*args, torch.from_numpy(row_token.astype(np.int32)).cuda(),
+                              torch.from_numpy(offsets.astype(np.int32)).cuda(), wq2, s8d, chd)
+    y_bad = W.wq_moe_gemm_w4a8(*args, torch.from_numpy(rt_bad).cuda(), torch.from_numpy(off_bad).cuda(),
+                               wq2, s8d, chd)
+    torch.cuda.synchronize()
+    a, b = host_bits16(y_ok), host_bits16(y_bad)
+    keep = np.setdiff1d(np.arange(R), bad_rows)
+    assert np.array_equal(a[keep], b[keep])
+    assert np.all(bf16_decode(b[bad_rows]) == 0.0)
+
+
 @pytest.mark.parametrize("T,E,K,N", [(700, 5, 384, 300), (64, 64, 256, 64)])
 def test_moe_gemm_identity_rows(W, T, E, K, N):
     _small_case(W, T, E, 1, K, N, seed=T * 3 + E, identity=True)

@@ -98,6 +98,29 @@ __device__ __forceinline__ void dequant16(u32x4_t w, scale_t<WDT> s, bf16x8_t ou
   }
 }
 
+// One 16-byte INT4 chunk (a 128-element step inside one scale group) of a
+// 16-column tile in the exact-code form, for a scale with a 5-bit significand
+// (int4_scale_short): then bf16(q * s) = q * s and
+//   x . bf16(q s) = s * (x . (q + 136) + x . (-136)).
+// The codes go to the MFMA as the exact bf16 patterns of q + 136 (no
+// conversion), a second MFMA chain against the constant -136 removes the
+// offset, and the fp32 sum of the group is scaled once.  The two chains take
+// the same x fragments in the same order into separate accumulators, so for
+// all-zero codes they are exact negatives and the chunk adds exactly zero.
+__device__ __forceinline__ void mma_int4_exact_codes(const bf16x8_t xa[4], u32x4_t wv, float s, f32x4_t& acc) {
+  const bf16x8_t neg136 = as_bf16x8(kBf16Neg136x2, kBf16Neg136x2, kBf16Neg136x2, kBf16Neg136x2);
+  f32x4_t pq = f32x4_t{0.f, 0.f, 0.f, 0.f}, pc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    uint32_t o[4];
+    dq_int4_word_o136(wv[j], o);
+    pq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[j], as_bf16x8(o[0], o[1], o[2], o[3]), pq, 0, 0, 0);
+    pc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[j], neg136, pc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; i++) acc[i] = __builtin_fmaf(s, pq[i] + pc[i], acc[i]);
+}
+
 // ---------------------------------------------------------------------------
 // Decode GEMV
 // ---------------------------------------------------------------------------
@@ -938,19 +961,7 @@ __device__ __forceinline__ void gemv_ring_tile(const uint16_t* __restrict__ x, i
         xa[j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(
             xrow + (XS ? (c % NS) * SLOT + (EPL * g + 8 * j) * 2 : (c * KSTEP + EPL * g + 8 * j) * 2)));
       if constexpr (FASTQ) {
-        if constexpr (WDT == W_INT4) {
-          const bf16x8_t neg136 = as_bf16x8(kBf16Neg136x2, kBf16Neg136x2, kBf16Neg136x2, kBf16Neg136x2);
-          f32x4_t pq = f32x4_t{0.f, 0.f, 0.f, 0.f}, pc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int j = 0; j < MF; j++) {
-            uint32_t o[4];
-            dq_int4_word_o136(wv[j], o);
-            pq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[j], as_bf16x8(o[0], o[1], o[2], o[3]), pq, 0, 0, 0);
-            pc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[j], neg136, pc, 0, 0, 0);
-          }
-#pragma unroll
-          for (int i = 0; i < 4; i++) acc[i] = __builtin_fmaf(scv, pq[i] + pc[i], acc[i]);
-        }
+        if constexpr (WDT == W_INT4) mma_int4_exact_codes(xa, wv, scv, acc);
       } else {
         bf16x8_t b[4];
         dequant16<WDT>(wv, scv, b);
@@ -960,15 +971,10 @@ __device__ __forceinline__ void gemv_ring_tile(const uint16_t* __restrict__ x, i
     }
   };
   // INT4 groups of 128: a step covers one group per row.  When every scale of
-  // the wave's slice has a 5-bit significand, bf16(q * s) = q * s, so
-  // x . bf16(q s) = s * (x . (q + 136) + x . (-136)): the codes go to the MFMA
-  // as the exact bf16 patterns of q + 136 (no conversion), a second MFMA chain
-  // against the constant -136 removes the offset, and the fp32 group sum is
-  // scaled once.  The two chains take the same x fragments in the same order
-  // into separate accumulators, so for all-zero codes they are exact negatives
-  // of each other and the group adds exactly zero.  Otherwise every weight is
-  // converted to bf16(q s).  The choice waits for the first step's loads (the
-  // scales were issued before them), as the first step would.
+  // the wave's slice has a 5-bit significand, every step takes the exact-code
+  // form (mma_int4_exact_codes); otherwise every weight is converted to
+  // bf16(q s).  The choice waits for the first step's loads (the scales were
+  // issued before them), as the first step would.
   if constexpr (WDT == W_INT4 && gs == 7) {
     wait_vm_n(REGW ? SPWE - 1 : (R - 1 < SPWE ? R - 1 : SPWE - 1) * VMS);
     bool mine = true;
@@ -1280,21 +1286,43 @@ __global__ __launch_bounds__(64 * WW) __attribute__((amdgpu_waves_per_eu(WW / 4,
   f32x4_t acc[CTW];
 #pragma unroll
   for (int t = 0; t < CTW; t++) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto run_steps = [&](auto fast_tag) {
+    constexpr bool FASTQ = decltype(fast_tag)::value;
 #pragma unroll
-  for (int c = 0; c < SPW; c++) {
-    bf16x8_t xa[MF];
+    for (int c = 0; c < SPW; c++) {
+      bf16x8_t xa[MF];
 #pragma unroll
-    for (int j = 0; j < MF; j++) {
-      const uint32_t q = (c * KSTEP + EPL * g + 8 * j) / 8;
-      xa[j] = as_bf16x8(ld16(xrow + 16 * (q ^ (uint32_t)(xtr & 15))));
+      for (int j = 0; j < MF; j++) {
+        const uint32_t q = (c * KSTEP + EPL * g + 8 * j) / 8;
+        xa[j] = as_bf16x8(ld16(xrow + 16 * (q ^ (uint32_t)(xtr & 15))));
+      }
+#pragma unroll
+      for (int t = 0; t < CTW; t++) {
+        if constexpr (FASTQ && WDT == W_INT4) {
+          mma_int4_exact_codes(xa, wr[c][t], bf16_to_f32(svr[c][t]), acc[t]);
+        } else {
+          bf16x8_t bq[4];
+          dequant16<WDT>(wr[c][t], scale_from_raw<WDT>(WDT == W_FP8 ? 0u : svr[c][t]), bq);
+#pragma unroll
+          for (int j = 0; j < MF; j++) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[j], bq[j], acc[t], 0, 0, 0);
+        }
+      }
     }
+  };
+  // INT4 groups of 128: the exact-code form when every scale of the wave's
+  // steps and tiles has a 5-bit significand (decided once the scales, issued
+  // before the weights, have landed)
+  if constexpr (WDT == W_INT4 && gs == 7) {
+    wait_vm<SPW * CTW>();
+    bool mine = true;
 #pragma unroll
-    for (int t = 0; t < CTW; t++) {
-      bf16x8_t bq[4];
-      dequant16<WDT>(wr[c][t], scale_from_raw<WDT>(WDT == W_FP8 ? 0u : svr[c][t]), bq);
+    for (int c = 0; c < SPW; c++)
 #pragma unroll
-      for (int j = 0; j < MF; j++) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[j], bq[j], acc[t], 0, 0, 0);
-    }
+      for (int t = 0; t < CTW; t++) mine &= int4_scale_short(svr[c][t]);
+    if (__builtin_amdgcn_ballot_w64(!mine) == 0) run_steps(std::true_type{});
+    else run_steps(std::false_type{});
+  } else {
+    run_steps(std::false_type{});
   }
 
   // acc[t][i] holds C[m = 4g + i][n = nl] of column tile t; the WW wave
@@ -1332,16 +1360,40 @@ constexpr int RING_NW = 4;
 // WQ_GROUP_ROWS rows (17-32 rows share each converted weight fragment between
 // two 16-row MFMA groups)
 constexpr int WQ_DECODE_ROWS = 64, WQ_GROUP_ROWS = 32;
-// 64 < M <= 256: the prefill kernel runs ceil(M/256) ceil(N/256) workgroups of
-// one 256x256 tile, each taking about 22 ns per element of K (90 us at
-// K = 4096), in rounds of one workgroup per CU; the decode launches of 32 rows
-// stream the weights at about 1.5 TB/s each.  Rows go through the decode forms
-// when that estimate is the smaller (at small N and large K the prefill grid
-// leaves most CUs idle).
-inline bool decode_rows_pay(int64_t M, int64_t N, int64_t K, int bits, int ncu) {
+// 64 < M <= 256: rows go through the decode launches when this cost model
+// says they finish first (at small N and large K the prefill grid leaves most
+// CUs idle).  Prefill: ceil(M/256) ceil(N/256) workgroups of one 256x256
+// tile, in rounds of one per CU, each tile taking 2 * 256 * 256 * K flops at
+// kPrefillTileEff of one CU's bf16 MFMA rate (1024 flops per clock per SIMD,
+// 4 SIMDs, at the device's clock).  Decode: one launch per 32 rows, each
+// streaming the packed weights at kDecodeRowsHbmFrac of the HBM peak.  The two
+// efficiencies are measured on MI355X (a 256x256 tile at K = 4096 takes about
+// 90 us: 0.606 of the CU rate; a 32-row launch moves 29.4 MB in about 20 us:
+// 0.1875 of 8 TB/s); the CU count and clock come from the device.
+constexpr double kPrefillTileEff = 0.606, kDecodeRowsHbmFrac = 0.1875, kHbmPeakBytesPerS = 8.0e12;
+struct DeviceRates { int ncu; double clk_hz; };
+hipError_t device_rates(DeviceRates* out) {
+  static DeviceRates cached[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64 && cached[dev].ncu > 0) {
+    *out = cached[dev];
+    return hipSuccess;
+  }
+  int ncu = 0, khz = 0;
+  if ((e = cu_count(&ncu)) != hipSuccess) return e;
+  if ((e = hipDeviceGetAttribute(&khz, hipDeviceAttributeClockRate, dev)) != hipSuccess) return e;
+  DeviceRates r{ncu, khz > 0 ? khz * 1e3 : 2.4e9};
+  if (dev >= 0 && dev < 64) cached[dev] = r;
+  *out = r;
+  return hipSuccess;
+}
+inline bool decode_rows_pay(int64_t M, int64_t N, int64_t K, int bits, const DeviceRates& r) {
   const int64_t wgs = ((M + 255) / 256) * ((N + 255) / 256);
-  const double t_pre = (double)((wgs + ncu - 1) / ncu) * (double)K * 0.022;        // us
-  const double t_dec = (double)((M + 31) / 32) * (double)N * (double)K * bits / 8 / 1.5e6;
+  const double tile_s = 2.0 * 256 * 256 * (double)K / (4.0 * 1024.0 * r.clk_hz * kPrefillTileEff);
+  const double t_pre = (double)((wgs + r.ncu - 1) / r.ncu) * tile_s;
+  const double t_dec = (double)((M + 31) / 32) * (double)N * (double)K * bits / 8 / (kDecodeRowsHbmFrac * kHbmPeakBytesPerS);
   return t_dec < t_pre;
 }
 constexpr int RING_DEPTH = 2;
@@ -1569,13 +1621,11 @@ wq_status wq_gemm(const void* x_bf16, int64_t M, int64_t N, int64_t K, const voi
   // to 32 rows, each streaming the weights once (about 20 us per 32 rows
   // there).
   bool rows = M <= WQ_DECODE_ROWS;
-#ifndef WQ_OLD_RULE
   if (!rows && M <= 256) {
-    int ncu = 0;
-    if (cu_count(&ncu) != hipSuccess) return WQ_EHIP;
-    rows = decode_rows_pay(M, N, K, wdt == W_FP8 ? 8 : 4, ncu);
+    DeviceRates dr{};
+    if (device_rates(&dr) != hipSuccess) return WQ_EHIP;
+    rows = decode_rows_pay(M, N, K, wdt == W_FP8 ? 8 : 4, dr);
   }
-#endif
   if (rows) {
     for (int64_t m0 = 0; m0 < M; m0 += WQ_GROUP_ROWS) {
       const int64_t mg = M - m0 < WQ_GROUP_ROWS ? M - m0 : WQ_GROUP_ROWS;

@@ -234,7 +234,7 @@ constexpr int MWN = 8, MTN = MBN / MWN, MMI = MBM / 32;
 
 __global__ __launch_bounds__(512) void k_moe_gemm(const uint8_t* __restrict__ x8, int64_t T,
                                                   const float* __restrict__ a_scale,
-                                                  const int32_t* __restrict__ row_token,
+                                                  const int32_t* __restrict__ row_token, int64_t R,
                                                   const int32_t* __restrict__ offsets, int E, int64_t N, int64_t K,
                                                   const uint32_t* __restrict__ wq, const uint8_t* __restrict__ s8,
                                                   const float* __restrict__ ch, uint16_t* __restrict__ y,
@@ -258,7 +258,11 @@ __global__ __launch_bounds__(512) void k_moe_gemm(const uint8_t* __restrict__ x8
     int before = 0;
     for (int e0 = 0; e0 < E; e0 += 64) {
       const int e = e0 + lane;
-      const int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
+      // the expert's rows [lo, hi), clamped to [0, R] whatever the caller's
+      // offsets hold (decreasing or out-of-range offsets give empty experts)
+      const int64_t lo = e < E ? (offsets[e] < 0 ? 0 : (offsets[e] > R ? R : offsets[e])) : 0;
+      const int64_t hi = e < E ? (offsets[e + 1] < lo ? lo : (offsets[e + 1] > R ? R : offsets[e + 1])) : 0;
+      const int cnt = (int)(hi - lo);
       const int tiles = (cnt + MBM - 1) / MBM;
       int incl = tiles;
       for (int o = 1; o < 64; o <<= 1) {
@@ -276,8 +280,10 @@ __global__ __launch_bounds__(512) void k_moe_gemm(const uint8_t* __restrict__ x8
   __syncthreads();
   const int e = tinfo[0];
   if (e < 0) return;                                    // whole workgroup
-  const int64_t r0 = offsets[e] + (int64_t)tinfo[1] * MBM;
-  const int64_t r1 = offsets[e + 1] < r0 + MBM ? offsets[e + 1] : r0 + MBM;
+  const int64_t elo = offsets[e] < 0 ? 0 : (offsets[e] > R ? R : offsets[e]);
+  const int64_t ehi = offsets[e + 1] < elo ? elo : (offsets[e + 1] > R ? R : offsets[e + 1]);
+  const int64_t r0 = elo + (int64_t)tinfo[1] * MBM;
+  const int64_t r1 = ehi < r0 + MBM ? ehi : r0 + MBM;
   const int64_t n0 = (int64_t)tn * MBN;
   const int64_t rowbytes = K / 2;
   const int64_t nrows = N - n0 < MBN ? N - n0 : MBN;
@@ -286,7 +292,9 @@ __global__ __launch_bounds__(512) void k_moe_gemm(const uint8_t* __restrict__ x8
   const int64_t G = K / 128;
   if (tid < MBM) {
     const int64_t gr = r0 + tid;
-    rscale[tid] = gr < r1 ? a_scale[row_token ? row_token[gr] : gr] : 0.0f;
+    // a gathered token index outside [0, T) reads as a zero row with scale 0
+    const int64_t tok = gr < r1 ? (row_token ? (int64_t)row_token[gr] : gr) : -1;
+    rscale[tid] = tok >= 0 && tok < T ? a_scale[tok] : 0.0f;
   }
 
   // A: 4 DMA instructions per wave, 8 gathered rows each, 16-byte chunks
@@ -297,12 +305,8 @@ __global__ __launch_bounds__(512) void k_moe_gemm(const uint8_t* __restrict__ x8
     const int r = 8 * (wave * 4 + i) + (lane >> 3);
     const int c = (lane & 7) ^ maswz(r);
     const int64_t gr = r0 + r;
-    if (gr < r1) {
-      const int64_t tok = row_token ? row_token[gr] : gr;
-      a_off[i] = (uint32_t)(tok * K) + 16 * c;
-    } else {
-      a_off[i] = 0x80000000u;
-    }
+    const int64_t tok = gr < r1 ? (row_token ? (int64_t)row_token[gr] : gr) : -1;
+    a_off[i] = tok >= 0 && tok < T ? (uint32_t)(tok * K) + 16 * c : 0x80000000u;
   }
   // B: 2 DMA instructions per wave, 16 rows of 64 bytes each, chunks swizzled
   uint32_t b_off[2];
@@ -482,7 +486,7 @@ wq_status wq_moe_gemm_w4a8(const uint8_t* x8, int64_t T, const float* a_scale, c
   const int64_t tiles_n = (N + MBN - 1) / MBN;
   if (tiles_m * tiles_n > 0x7FFFFFFFLL) return WQ_EINVAL;
   k_moe_gemm<<<(unsigned)(tiles_m * tiles_n), 512, MLDS, (hipStream_t)stream>>>(
-      x8, T, a_scale, row_token, offsets, experts, N, K, wq, s8, ch, y, (int)tiles_n);
+      x8, T, a_scale, row_token, R, offsets, experts, N, K, wq, s8, ch, y, (int)tiles_n);
   return wq_launch_status();
 }
 
