@@ -29,7 +29,8 @@ out where sysfs does not expose them).
 --only CASE runs a single case without the full summary (for rocprofv3):
 decode (the same graph-timed steps as the headline, prints one short JSON
 line), decode_m4, decode_m16, decode_w8, decode_nvfp4, decode_asym, prefill, prefill_nvfp4, w8a8_block, w8a8_channel, quant_e4m3, quant_mxfp4, quant_mxfp8, wquant_mxfp4, copy,
-moe_gate_up, moe_down.
+moe_gate_up, moe_down, stream_decode (the read-only stream of the decode weight
+copies), stream_2g, torch_matmul (hipBLASLt on the dequantized prefill weights).
 """
 from __future__ import annotations
 
@@ -531,6 +532,22 @@ class MoeW4A8:
         self.W.wq_moe_gemm_w4a8(self.x8, self.a, self.rt, self.off, self.wq, self.s8, self.ch, y=self.y)
 
 
+class TorchMatmul:
+    """torch.matmul (hipBLASLt) of the prefill activations with the dequantized
+    MXFP4 weights of the prefill workload (the bf16 GEMM the kernel is
+    compared with)."""
+
+    def __init__(self, torch, W):
+        pf = Prefill(torch, W)
+        self.torch, self.x = torch, pf.x
+        self.wb = W.wq_dequant(pf.codes, W.WQ_E2M1X2, pf.sc, W.WQ_E8M0, 32, pf.N, pf.K)
+        self.flops = pf.flops
+        del pf
+
+    def launch(self, i):
+        self.torch.matmul(self.x, self.wb.t())
+
+
 class Copy:
     """Streaming copy of 256 MiB (read + write) as a secondary HBM denominator."""
 
@@ -610,9 +627,11 @@ def main():
               "quant_mxfp8": lambda: ActQuant(torch, W, "mxfp8"),
               "wquant_mxfp4": lambda: WeightQuant(torch, W),
               "moe_gate_up": lambda: MoeW4A8(torch, W, "gate_up"), "moe_down": lambda: MoeW4A8(torch, W, "down"),
-              "stream_decode": lambda: Decode(torch, W, 1), "stream_2g": lambda: BigStream(torch, W)}[case]
+              "stream_decode": lambda: Decode(torch, W, 1), "stream_2g": lambda: BigStream(torch, W),
+              "torch_matmul": lambda: TorchMatmul(torch, W)}[case]
         obj = mk()
-        big = case in ("prefill", "prefill_nvfp4", "moe_gate_up", "moe_down", "w8a8_block", "w8a8_channel")
+        big = case in ("prefill", "prefill_nvfp4", "moe_gate_up", "moe_down", "w8a8_block", "w8a8_channel",
+                       "torch_matmul")
         reps = args.reps or (20 if big else 100)
         # the clocks settle over the first launches of a large kernel: the
         # profile's median then reflects the steady state, as the timed runs do
