@@ -109,7 +109,8 @@ class Region:
     region's launches while the device is still busy and the submission
     latency stays off the clock: event a fires when the busy kernel ends, and
     the first launch follows at once.  The busy kernel's iteration count is
-    sized from a measured rate to last about twice the host's submission time.
+    sized from a measured rate to last about four times the host's submission
+    time.
     `rounds` regions are timed; ms per launch is their median."""
 
     def __init__(self, torch, W, enqueue, launches, rounds=5):
@@ -125,7 +126,7 @@ class Region:
         enqueue()                                   # untimed pass: host submission time
         self.host_ms = (time.perf_counter() - t) * 1e3
         torch.cuda.synchronize()
-        self.iters = int(min(max(2.0 * max(self.host_ms, 0.05) / self.ms_per_iter, 1000), 1 << 24))
+        self.iters = int(min(max(4.0 * max(self.host_ms, 0.05) / self.ms_per_iter, 1000), 1 << 24))
         self.windows = []
 
     def run(self, sampler=None):

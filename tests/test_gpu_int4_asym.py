@@ -10,7 +10,7 @@ from oracle import gemm as OG
 from oracle import int4_asym as OA
 from oracle.formats import bf16_decode
 from synthetic import all_bf16_patterns, bf16_bits_to_f32, decode_inputs, prefill_inputs, to_bf16_bits
-from tests.gpu_helpers import banner, dev_bf16, dev_f32, dev_words, host_bits16, host_words
+from tests.gpu_helpers import banner, check_all_rows, dev_bf16, dev_f32, dev_words, host_bits16, host_words
 
 pytestmark = pytest.mark.gpu
 
@@ -142,14 +142,12 @@ def test_decode_full_size(W, decode_asym, M):
     _check(y, xbits, wdeq)
 
 
-def test_prefill_full_size_sampled_rows(W):
+def test_prefill_full_size_all_rows(W):
     xbits, Wf = prefill_inputs(0)
     args, wdeq = _args(W, Wf, 128)
-    banner("prefill asymmetric int4 full size 8192x4096 . 14336x4096")
+    banner("prefill asymmetric int4 full size 8192x4096 . 14336x4096, all rows")
     y = W.wq_gemm(dev_bf16(xbits), *args, 14336)
-    rows = np.sort(np.random.default_rng(97).choice(8192, 160, replace=False))
-    rows = np.unique(np.concatenate([rows, [0, 255, 256, 8191]]))
-    _check(y, xbits, wdeq, rows=rows)
+    check_all_rows(y, xbits, wdeq)
 
 
 def test_zero_point_shifts_the_result(W):

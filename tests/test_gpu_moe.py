@@ -198,6 +198,41 @@ def test_moe_gemm_small(W, T, E, k, K, N):
     _small_case(W, T, E, k, K, N, seed=T + E + k + K + N)
 
 
+def test_moe_gemm_subnormal_group_scales(W):
+    # Groups whose INT4 scale sits ~10^4 below the channel's largest: their
+    # fp8 scale (56 * s / max s) lands in the E4M3 subnormal range and so do
+    # many table entries q * s8, which the fp8 matrix cores read as zero.  The
+    # result must stay within the bound of the exact-operand reference; the
+    # size of the flushed terms is printed for the record.
+    g = np.random.default_rng(21)
+    E, T, K, N = 2, 96, 512, 64
+    R = T
+    offsets = np.array([0, 40, R], np.int32)
+    xbits = to_bf16_bits(g.standard_normal((T, K)).astype(np.float32))
+    x8, a_s = OW.quantize_tokens(xbits)
+    experts, packed, sbits = [], [], []
+    for e in range(E):
+        Wf = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
+        Wf[:, 128:] *= 1e-4                                    # groups 1-3 of every row
+        p, sb, _ = OI.quantize_int4(Wf, 128)
+        s8, ch = OW.scale_recipe(sb)
+        assert np.all((s8[:, 1:] & 0x78) == 0)                 # subnormal fp8 group scales
+        experts.append((p, s8, ch))
+        packed.append(p)
+        sbits.append(sb)
+    banner("moe gemm subnormal group scales")
+    wq2, s8d, chd = W.wq_w4a8_prepack(dev_words(np.stack(packed)), dev_bf16(np.stack(sbits)))
+    y = W.wq_moe_gemm_w4a8(dev_u8(x8), dev_f32(a_s), None, torch.from_numpy(offsets).cuda(), wq2, s8d, chd)
+    yv = bf16_decode(host_bits16(y))
+    ref, asum = OW.grouped_gemm_reference(x8, a_s, offsets, np.arange(R), experts, 128)
+    ratio = OG.worst_ratio(yv, ref, asum)
+    dev = float(np.max(np.abs(yv - ref) / np.maximum(asum, 1e-30)))
+    print(f"[w4a8 subnormal group scales] worst error / bound {ratio:.4f}, max |y - ref| / sum|x w| {dev:.2e}",
+          flush=True)
+    assert np.isfinite(yv).all()
+    assert ratio <= 1.0, f"worst error / bound = {ratio:.3f}"
+
+
 def test_moe_gemm_clamps_device_offsets_and_tokens(W):
     # offsets and row_token are device data the host cannot validate: the
     # kernel clamps every expert's rows to [0, R] and reads a token index
@@ -243,7 +278,13 @@ def test_moe_gemm_identity_rows(W, T, E, K, N):
 # ---------------------------------------------------------------------------
 # full size (64 experts, 4096 tokens, top 8), sampled rows
 # ---------------------------------------------------------------------------
-CHECKED = (0, 17, 42, 63)
+def _checked_rows(lo, hi):
+    """First and last grouped row of an expert and the rows on both sides of
+    each of its 256-row tile boundaries."""
+    rows = {lo, hi - 1}
+    for b in range(lo + 256, hi, 256):
+        rows |= {b - 1, b}
+    return np.array(sorted(r for r in rows if lo <= r < hi))
 
 
 def _full_size(W, which, pool):
@@ -261,12 +302,8 @@ def _full_size(W, which, pool):
         x_dev = moe_down_input_gpu(rows=R, inter=inter)
     x8, a_s = W.quantize_e4m3(x_dev, -1)
     a_s = a_s.reshape(-1).contiguous()
-    rng = np.random.default_rng(5)
-    sampled = {}
-    for e in CHECKED:
-        lo, hi = int(offsets[e]), int(offsets[e + 1])
-        pick = {lo, hi - 1, min(lo + 255, hi - 1), min(lo + 256, hi - 1)} | set(rng.integers(lo, hi, 4).tolist())
-        sampled[e] = np.array(sorted(pick))
+    sampled = {e: _checked_rows(int(offsets[e]), int(offsets[e + 1])) for e in range(E)
+               if offsets[e + 1] > offsets[e]}
     xrows = {}
     for e, rows in sampled.items():
         toks = row_token[rows] if which == "gate_up" else rows
@@ -275,14 +312,15 @@ def _full_size(W, which, pool):
         x8[torch.from_numpy(toks).cuda()] = dev_u8(c)
         a_s[torch.from_numpy(toks).cuda()] = dev_f32(s)
         xrows[e] = (c, s)
-    # weights: GPU-generated; the checked experts quantized by the oracle
-    banner("moe full size", which, "weights")
+    # weights: GPU-generated, every expert quantized by the oracle (in worker
+    # processes), so that every checked output comes from oracle-made inputs
+    banner("moe full size", which, "weights of", E, "experts")
     packed = torch.empty((E, N, K // 8), dtype=torch.int32, device="cuda")
     sbits = torch.empty((E, N, K // 128), dtype=torch.bfloat16, device="cuda")
     futures = {}
     for e in range(E):
         Wf = moe_expert_weight_gpu(e, which)
-        if e in CHECKED:
+        if e in sampled:
             futures[e] = pool.submit(moe_workers.expert_case, Wf.cpu().numpy(), *xrows[e])
         else:
             W.quantize_int4(Wf, 128, packed=packed[e], scales=sbits[e])
@@ -297,7 +335,7 @@ def _full_size(W, which, pool):
         assert R == T * k
     y = W.wq_moe_gemm_w4a8(x8, a_s, rt, torch.from_numpy(offsets.astype(np.int32)).cuda(), wq2, s8, ch)
     torch.cuda.synchronize()
-    worst = 0.0
+    worst, nrows = 0.0, 0
     for e, rows in sampled.items():
         _, _, s8_o, ch_o, ref, asum = results[e]
         assert np.array_equal(host_u8(s8[e]), s8_o)
@@ -305,15 +343,17 @@ def _full_size(W, which, pool):
         yv = bf16_decode(host_bits16(y[torch.from_numpy(rows).cuda()]))
         assert np.isfinite(yv).all()
         worst = max(worst, OG.worst_ratio(yv, ref, asum))
+        nrows += len(rows)
+    assert len(sampled) == E and nrows >= 4 * E
     assert worst <= 1.0, f"worst error / bound = {worst:.3f}"
 
 
 @pytest.fixture(scope="module")
 def pool():
-    with ProcessPoolExecutor(max_workers=len(CHECKED), mp_context=mp.get_context("spawn")) as ex:
+    with ProcessPoolExecutor(max_workers=8, mp_context=mp.get_context("spawn")) as ex:
         yield ex
 
 
 @pytest.mark.parametrize("which", ["gate_up", "down"])
-def test_moe_full_size_sampled_rows(W, pool, which):
+def test_moe_full_size_every_expert(W, pool, which):
     _full_size(W, which, pool)

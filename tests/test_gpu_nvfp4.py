@@ -10,7 +10,7 @@ from oracle import gemm as OG
 from oracle import nvfp4 as ON
 from oracle.formats import bf16_decode
 from synthetic import all_bf16_patterns, bf16_bits_to_f32, decode_inputs, prefill_inputs, to_bf16_bits
-from tests.gpu_helpers import banner, dev_bf16, dev_f32, dev_u8, host_bits16, host_u8
+from tests.gpu_helpers import banner, check_all_rows, dev_bf16, dev_f32, dev_u8, host_bits16, host_u8
 
 pytestmark = pytest.mark.gpu
 
@@ -171,15 +171,13 @@ def test_decode_full_size(W, decode_nv, M):
     _check(y, xbits, wdeq, g)
 
 
-def test_prefill_full_size_sampled_rows(W):
+def test_prefill_full_size_all_rows(W):
     xbits, Wf = prefill_inputs(0)
     g = tensor_scale(Wf)
     args, wdeq = _nv_args(W, Wf, g)
-    banner("prefill nvfp4 full size 8192x4096 . 14336x4096")
+    banner("prefill nvfp4 full size 8192x4096 . 14336x4096, all rows")
     y = W.wq_gemm(dev_bf16(xbits), *args, 14336, alpha=g)
-    rows = np.sort(np.random.default_rng(98).choice(8192, 160, replace=False))
-    rows = np.unique(np.concatenate([rows, [0, 255, 256, 8191]]))
-    _check(y, xbits, wdeq, g, rows=rows)
+    check_all_rows(y, xbits, wdeq, np.full(wdeq.shape[0], g))
 
 
 def test_alpha_scales_the_output(W):
