@@ -28,7 +28,7 @@ out where sysfs does not expose them).
 
 --only CASE runs a single case without the full summary (for rocprofv3):
 decode (the same graph-timed steps as the headline, prints one short JSON
-line), decode_m4, decode_m16, decode_w8, decode_nvfp4, decode_asym, prefill, prefill_nvfp4, w8a8_block, w8a8_channel, quant_e4m3, quant_mxfp4, quant_mxfp8, wquant_mxfp4, copy,
+line), decode_m1 (the headline's launches, eager, for counter runs), decode_m4, decode_m16, decode_w8, decode_nvfp4, decode_asym, prefill, prefill_nvfp4, w8a8_block, w8a8_channel, quant_e4m3, quant_mxfp4, quant_mxfp8, wquant_mxfp4, copy,
 moe_gate_up, moe_down, stream_decode (the read-only stream of the decode weight
 copies), stream_2g, torch_matmul (hipBLASLt on the dequantized prefill weights).
 """
@@ -111,7 +111,9 @@ class Region:
     the first launch follows at once.  The busy kernel's iteration count is
     sized from a measured rate to last about four times the host's submission
     time.
-    `rounds` regions are timed; ms per launch is their median."""
+    `rounds` regions are timed; ms per launch is their median.  A one-wave
+    clock probe (wq_util_clock) runs just before event a and just after event
+    b and records the shader clock at each end of every region."""
 
     def __init__(self, torch, W, enqueue, launches, rounds=5):
         self.torch, self.W, self.enqueue, self.launches, self.rounds = torch, W, enqueue, launches, rounds
@@ -128,18 +130,22 @@ class Region:
         torch.cuda.synchronize()
         self.iters = int(min(max(4.0 * max(self.host_ms, 0.05) / self.ms_per_iter, 1000), 1 << 24))
         self.windows = []
+        self.clk = torch.zeros((rounds, 2, 2), dtype=torch.int64, device="cuda")
+        self.wall_khz = W.wq_util_wall_clock_khz()
 
     def run(self, sampler=None):
         torch = self.torch
         ms, covered = [], []
-        for _ in range(self.rounds):
+        for r in range(self.rounds):
             torch.cuda.synchronize()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             t0 = time.perf_counter()
             self.W.wq_util_spin(self.iters)
+            self.W.wq_util_clock(self.clk[r, 0])
             a.record()
             self.enqueue()
             b.record()
+            self.W.wq_util_clock(self.clk[r, 1])
             t1 = time.perf_counter()
             b.synchronize()
             t2 = time.perf_counter()
@@ -150,13 +156,17 @@ class Region:
             self.windows.append((t0, t2))
         self.ms_rounds = ms
         self.covered = all(covered)
+        c = self.clk.cpu().numpy().astype(np.float64)
+        self.mhz = c[:, :, 0] / np.maximum(c[:, :, 1], 1) * self.wall_khz * 1e-3
         return float(np.median(ms))
 
     def describe(self):
         return {"rounds_us_per_launch": [round(m * 1e3, 3) for m in self.ms_rounds],
                 "median_of_rounds": len(self.ms_rounds), "launches_per_round": self.launches,
                 "busy_kernel_us": round(self.iters * self.ms_per_iter * 1e3, 1),
-                "host_submit_us": round(self.host_ms * 1e3, 1), "busy_kernel_covered_submission": self.covered}
+                "host_submit_us": round(self.host_ms * 1e3, 1), "busy_kernel_covered_submission": self.covered,
+                "shader_clock_mhz": {"before_region": [round(v) for v in self.mhz[:, 0]],
+                                     "after_region": [round(v) for v in self.mhz[:, 1]]}}
 
 
 class ClockSampler:
@@ -378,8 +388,9 @@ class BigStream:
 
 
 class Prefill:
-    """x[8192, 4096] . dequant(W[14336, 4096])^T with MXFP4 (E8M0 per 32) or
-    NVFP4 (E4M3 per 16 and a per-tensor scale) weights."""
+    """x[8192, 4096] . dequant(W[14336, 4096])^T with MXFP4 (E8M0 per 32),
+    NVFP4 (E4M3 per 16 and a per-tensor scale) or symmetric INT4 (bf16 scale
+    per 128) weights."""
 
     def __init__(self, torch, W, M=8192, K=4096, N=14336, kind="mxfp4"):
         from synthetic import prefill_inputs
@@ -391,6 +402,11 @@ class Prefill:
             self.alpha = nvfp4_tensor_scale(torch, wdev)
             self.codes, self.sc = W.quantize_nvfp4(wdev, self.alpha)
             self.meta = (W.WQ_E2M1X2, W.WQ_E4M3, 16)
+        elif kind == "int4":
+            self.alpha = 1.0
+            packed, self.sc = W.quantize_int4(wdev, 128)
+            self.codes = packed.view(torch.uint8)
+            self.meta = (W.WQ_INT4X8, W.WQ_BF16, 128)
         else:
             self.alpha = 1.0
             self.codes, self.sc = W.quantize_mxfp4(wdev, 32)
@@ -398,7 +414,8 @@ class Prefill:
         del wdev
         self.y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
         self.flops = 2.0 * M * N * K
-        self.bytes = self.codes.numel() + self.sc.numel() + M * K * 2 + M * N * 2
+        self.bytes = (self.codes.numel() * self.codes.element_size() + self.sc.numel() * self.sc.element_size()
+                      + M * K * 2 + M * N * 2)
 
     def launch(self, i):
         wdt, sdt, grp = self.meta
@@ -619,9 +636,11 @@ def main():
     if args.only and args.only != "decode":
         case = args.only
         mk = {"decode_w8": lambda: Decode(torch, W, 1, "e4m3"), "decode_nvfp4": lambda: Decode(torch, W, 1, "nvfp4"),
+              "decode_m1": lambda: Decode(torch, W, 1),
               "decode_m16": lambda: Decode(torch, W, 16), "decode_m4": lambda: Decode(torch, W, 4),
               "decode_asym": lambda: Decode(torch, W, 1, "int4_asym"),
               "prefill_nvfp4": lambda: Prefill(torch, W, kind="nvfp4"),
+              "prefill_int4": lambda: Prefill(torch, W, kind="int4"),
               "w8a8_block": lambda: W8A8(torch, W, "block"), "w8a8_channel": lambda: W8A8(torch, W, "channel"),
               "prefill": lambda: Prefill(torch, W), "quant_e4m3": lambda: ActQuant(torch, W, "e4m3"),
               "quant_mxfp4": lambda: ActQuant(torch, W, "mxfp4"), "copy": lambda: Copy(torch),
@@ -631,7 +650,7 @@ def main():
               "stream_decode": lambda: Decode(torch, W, 1), "stream_2g": lambda: BigStream(torch, W),
               "torch_matmul": lambda: TorchMatmul(torch, W)}[case]
         obj = mk()
-        big = case in ("prefill", "prefill_nvfp4", "moe_gate_up", "moe_down", "w8a8_block", "w8a8_channel",
+        big = case in ("prefill", "prefill_nvfp4", "prefill_int4", "moe_gate_up", "moe_down", "w8a8_block", "w8a8_channel",
                        "torch_matmul")
         reps = args.reps or (20 if big else 100)
         # the clocks settle over the first launches of a large kernel: the

@@ -53,6 +53,27 @@ wq_status wq_util_stream_read(const void* buf, int64_t bytes, uint32_t magic, ui
  */
 wq_status wq_util_spin(int64_t iters, uint32_t magic, uint32_t* sink, void* stream);
 
+/*
+ * wq_util_clock -- one wave records the shader clock over a short interval:
+ * it reads the shader cycle counter and the constant-rate wall clock, polls
+ * the wall clock until `ticks` ticks have passed (or 2^20 polls, whichever
+ * comes first), reads both again and stores out[0] = cycles elapsed and
+ * out[1] = wall ticks elapsed.  The shader clock over the interval is
+ * out[0] / out[1] times the wall clock's rate (wq_util_wall_clock_khz).
+ *
+ * Enqueued just before and just after a timed region on the same stream, it
+ * records the clock that the region ran at (a clock set by power management
+ * changes over milliseconds; the region lasts a fraction of one).
+ *
+ * ticks  1 .. 2^20 wall-clock ticks (WQ_EINVAL otherwise).
+ * out    two device int64, 16-byte aligned (WQ_EALIGN), written by the kernel.
+ */
+wq_status wq_util_clock(int64_t ticks, int64_t* out, void* stream);
+
+/* wq_util_wall_clock_khz -- rate of the current device's wall clock (the
+ * counter wq_util_clock reads as out[1]) in kHz, written to *khz. */
+wq_status wq_util_wall_clock_khz(int* khz);
+
 #ifdef __cplusplus
 }
 #endif

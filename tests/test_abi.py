@@ -33,7 +33,8 @@ def test_header_declares_the_entry_points():
     for n in ("quantize_e4m3", "quantize_mxfp4", "quantize_mx", "quantize_nvfp4", "quantize_int4", "quantize_int4_asym", "wq_dequant", "wq_gemm",
               "wq_gemm_workspace_size", "wq_status_string", "wq_moe_route", "wq_w4a8_prepack",
               "wq_w4a8_dequant", "wq_moe_gemm_w4a8", "quantize_e4m3_static", "quantize_e4m3_block2d",
-              "wq_gemm_w8a8", "wq_util_stream_read", "wq_util_spin"):
+              "wq_gemm_w8a8", "wq_util_stream_read", "wq_util_spin", "wq_util_clock",
+              "wq_util_wall_clock_khz"):
         assert n in names
 
 
@@ -207,3 +208,14 @@ def test_utilities_reject_bad_arguments(lib):
     assert sp(0, 0, fake, None) == 1
     assert sp((1 << 24) + 1, 0, fake, None) == 1
     assert sp(100, 0, None, None) == 1
+    ck = lib.wq_util_clock
+    ck.restype = ctypes.c_int
+    ck.argtypes = [ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    assert ck(0, fake, None) == 1
+    assert ck((1 << 20) + 1, fake, None) == 1
+    assert ck(200, None, None) == 1
+    assert ck(200, fake + 8, None) == 2
+    wk = lib.wq_util_wall_clock_khz
+    wk.restype = ctypes.c_int
+    wk.argtypes = [ctypes.c_void_p]
+    assert wk(None) == 1

@@ -54,6 +54,8 @@ _SIGS = {
     "wq_moe_gemm_w4a8": ([_vp, _i64, _vp, _vp, _i64, _vp, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "wq_util_stream_read": ([_vp, _i64, ctypes.c_uint32, _vp, _vp], ctypes.c_int),
     "wq_util_spin": ([_i64, ctypes.c_uint32, _vp, _vp], ctypes.c_int),
+    "wq_util_clock": ([_i64, _vp, _vp], ctypes.c_int),
+    "wq_util_wall_clock_khz": ([ctypes.POINTER(ctypes.c_int)], ctypes.c_int),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -421,3 +423,19 @@ def wq_util_spin(iters: int, device=None) -> None:
     """Enqueue a bounded busy kernel of `iters` iterations (one workgroup per CU)."""
     dev = torch.device("cuda") if device is None else torch.device(device)
     _check(lib.wq_util_spin(int(iters), _MAGIC, _sink(dev).data_ptr(), _stream()), "wq_util_spin")
+
+
+def wq_util_clock(out: torch.Tensor, ticks: int = 200) -> None:
+    """Enqueue the one-wave clock probe; writes cycles and wall-clock ticks
+    elapsed over about `ticks` wall-clock ticks into the two int64 of `out`."""
+    _dev(out, "out")
+    if out.dtype != torch.int64 or out.numel() < 2 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous int64 device tensor of at least 2 elements")
+    _check(lib.wq_util_clock(int(ticks), out.data_ptr(), _stream()), "wq_util_clock")
+
+
+def wq_util_wall_clock_khz() -> int:
+    """Rate of the current device's wall clock in kHz."""
+    khz = ctypes.c_int(0)
+    _check(lib.wq_util_wall_clock_khz(ctypes.byref(khz)), "wq_util_wall_clock_khz")
+    return khz.value

@@ -43,6 +43,22 @@ __global__ __launch_bounds__(256) void k_spin(int64_t iters, uint32_t magic, uin
   if ((__float_as_uint(a) ^ __float_as_uint(b) ^ __float_as_uint(c) ^ __float_as_uint(d)) == magic) sink[0] = magic;
 }
 
+// One wave stamps the shader cycle counter (s_memtime) and the constant-rate
+// wall clock (s_memrealtime) at its start, polls the wall clock until `ticks`
+// ticks have passed (at most 2^20 polls), stamps both again and stores the
+// two differences: their ratio times the wall clock's rate is the shader
+// clock over that interval.
+__global__ __launch_bounds__(64) void k_clock(int64_t ticks, int64_t* __restrict__ out) {
+  const int64_t c0 = (int64_t)__builtin_amdgcn_s_memtime(), w0 = (int64_t)__builtin_amdgcn_s_memrealtime();
+  int64_t w = w0;
+  for (int i = 0; i < (1 << 20) && w - w0 < ticks; i++) w = (int64_t)__builtin_amdgcn_s_memrealtime();
+  const int64_t c1 = (int64_t)__builtin_amdgcn_s_memtime(), w1 = (int64_t)__builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) {
+    out[0] = c1 - c0;
+    out[1] = w1 - w0;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -63,6 +79,22 @@ wq_status wq_util_spin(int64_t iters, uint32_t magic, uint32_t* sink, void* stre
     return WQ_EHIP;
   k_spin<<<(unsigned)ncu, 256, 0, (hipStream_t)stream>>>(iters, magic, sink);
   return wq_launch_status();
+}
+
+wq_status wq_util_clock(int64_t ticks, int64_t* out, void* stream) {
+  if (!out || ticks < 1 || ticks > (int64_t(1) << 20)) return WQ_EINVAL;
+  if (!wq_aligned(out)) return WQ_EALIGN;
+  k_clock<<<1, 64, 0, (hipStream_t)stream>>>(ticks, out);
+  return wq_launch_status();
+}
+
+wq_status wq_util_wall_clock_khz(int* khz) {
+  int dev = 0;
+  if (!khz) return WQ_EINVAL;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
+      *khz <= 0)
+    return WQ_EHIP;
+  return WQ_OK;
 }
 
 }  // extern "C"
