@@ -192,8 +192,13 @@ def _small_case(W, T, E, k, K, N, seed, identity=False):
     assert ratio <= 1.0, f"worst error / bound = {ratio:.3f}"
 
 
+# K > 4096 (more than 32 groups: the kernel reloads its LDS copy of the group
+# scales every 32 steps), group counts that are and are not multiples of 4
+# (dword or byte loads of the scales), and experts of 1..256+ rows (partial
+# row tiles of every size class)
 @pytest.mark.parametrize("T,E,k,K,N", [(300, 8, 2, 512, 384), (20, 16, 1, 256, 100), (600, 4, 4, 1024, 520),
-                                       (1, 3, 2, 128, 33)])
+                                       (1, 3, 2, 128, 33), (150, 3, 2, 8448, 72), (90, 2, 2, 4224, 40),
+                                       (40, 2, 1, 5120, 64), (50, 3, 2, 640, 48)])
 def test_moe_gemm_small(W, T, E, k, K, N):
     _small_case(W, T, E, k, K, N, seed=T + E + k + K + N)
 

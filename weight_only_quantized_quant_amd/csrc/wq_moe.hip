@@ -30,6 +30,8 @@
 // operands as zero.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "wq.h"
 #include "wq_device.h"
 #include "wq_host.h"
@@ -218,6 +220,7 @@ constexpr int MB_TILE = MBN * MBK / 2;                  // 16 KB of packed INT4
 constexpr int MSTAGE = MA_TILE + MB_TILE;
 constexpr int MNSTAGE = 3;                              // loads run two steps ahead
 constexpr int MLDS = MNSTAGE * MSTAGE;                  // 144 KB
+constexpr int MS8_CHUNK = 32;                           // groups of s8 held in LDS at a time (8 KB)
 // LDS placement of the tiles' 16-byte chunks.  A ds_read_b128 serves 16
 // lanes per pass over 64 banks (256 bytes), so the 16 rows one fragment read
 // touches must land on distinct 16-byte bank groups.  Activation rows of 128
@@ -242,6 +245,7 @@ __global__ __launch_bounds__(512) void k_moe_gemm(const uint8_t* __restrict__ x8
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ int tinfo[2];
   __shared__ float rscale[MBM];                         // a_scale of each row of the tile
+  __shared__ uint8_t s8l[MS8_CHUNK * MBN];              // s8 of MS8_CHUNK groups x the tile's columns
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave;
@@ -284,6 +288,7 @@ __global__ __launch_bounds__(512) void k_moe_gemm(const uint8_t* __restrict__ x8
   const int64_t ehi = offsets[e + 1] < elo ? elo : (offsets[e + 1] > R ? R : offsets[e + 1]);
   const int64_t r0 = elo + (int64_t)tinfo[1] * MBM;
   const int64_t r1 = ehi < r0 + MBM ? ehi : r0 + MBM;
+  const int ntile = __builtin_amdgcn_readfirstlane((int)((r1 - r0 + 31) >> 5));   // 1 .. MMI row tiles
   const int64_t n0 = (int64_t)tn * MBN;
   const int64_t rowbytes = K / 2;
   const int64_t nrows = N - n0 < MBN ? N - n0 : MBN;
@@ -315,19 +320,50 @@ __global__ __launch_bounds__(512) void k_moe_gemm(const uint8_t* __restrict__ x8
     const int r = 16 * (wave * 2 + i) + (lane >> 2);
     b_off[i] = (uint32_t)(r * rowbytes) + 16 * ((lane & 3) ^ mbswz(r));
   }
+  // The step's K offset goes in the DMA's scalar offset: the per-lane offsets
+  // stay in registers that nothing in the loop writes (a row past the
+  // expert's end keeps its 0x80000000 offset, still past the buffer's end).
   auto issue = [&](int stage, int64_t k0) {
     uint8_t* A = lds + stage * MSTAGE;
     uint8_t* B = A + MA_TILE;
 #pragma unroll
-    for (int i = 0; i < 4; i++) lds_dma16(ra, A + (wave * 4 + i) * 1024, a_off[i] + (uint32_t)k0);
+    for (int i = 0; i < 4; i++) lds_dma16(ra, A + (wave * 4 + i) * 1024, a_off[i], (uint32_t)k0);
 #pragma unroll
-    for (int i = 0; i < 2; i++) lds_dma16(rb, B + (wave * 2 + i) * 1024, b_off[i] + (uint32_t)(k0 / 2));
+    for (int i = 0; i < 2; i++) lds_dma16(rb, B + (wave * 2 + i) * 1024, b_off[i], (uint32_t)(k0 / 2));
   };
 
-  // group scales of this lane's column
-  int64_t ncol = n0 + wn * MTN + l32;
-  ncol = ncol < N ? ncol : N - 1;
-  const uint8_t* s8row = s8 + ((int64_t)e * N + ncol) * G;
+  // Group scales: thread t < 256 copies column n0 + t's s8 codes of groups
+  // [g0, g0 + MS8_CHUNK) into s8l (group-major), so that the K loop reads them
+  // from LDS and issues no loads into registers (which would wait on the
+  // tile loads queued ahead of them).
+  const int myc = wn * MTN + l32;
+  auto load_s8_chunk = [&](int g0) {
+    if (tid < MBN) {
+      int64_t c = n0 + tid;
+      c = c < N ? c : N - 1;
+      const uint8_t* p = s8 + ((int64_t)e * N + c) * G + g0;
+      const int cnt = (int)(G - g0) < MS8_CHUNK ? (int)(G - g0) : MS8_CHUNK;
+      if (G % 4 == 0) {                                 // 4-byte aligned rows: dword loads
+        const uint32_t* p4 = reinterpret_cast<const uint32_t*>(p);
+        uint32_t v[MS8_CHUNK / 4];
+#pragma unroll
+        for (int q = 0; q < MS8_CHUNK / 4; q++) v[q] = 4 * q < cnt ? p4[q] : 0u;
+#pragma unroll
+        for (int q = 0; q < MS8_CHUNK / 4; q++)
+          if (4 * q < cnt)
+#pragma unroll
+            for (int b = 0; b < 4; b++) s8l[(4 * q + b) * MBN + tid] = (uint8_t)(v[q] >> (8 * b));
+      } else {
+        uint8_t v[MS8_CHUNK];
+#pragma unroll
+        for (int q = 0; q < MS8_CHUNK; q++) v[q] = p[q < cnt ? q : cnt - 1];   // entries past G: unused
+#pragma unroll
+        for (int q = 0; q < MS8_CHUNK; q++) s8l[q * MBN + tid] = v[q];
+      }
+    }
+  };
+  // raw s8 of step k (its chunk resident)
+  auto s8_of = [&](int k) -> uint32_t { return s8l[(k % MS8_CHUNK) * MBN + myc]; };
 
   f32x16_t acc[MMI];
 #pragma unroll
@@ -352,13 +388,16 @@ __global__ __launch_bounds__(512) void k_moe_gemm(const uint8_t* __restrict__ x8
     const u32x4_t p1 = ld16(A + r * 128 + (((c0 + 1) ^ maswz(r)) << 4));
     return i32x8_t{(int)p0[0], (int)p0[1], (int)p0[2], (int)p0[3], (int)p1[0], (int)p1[1], (int)p1[2], (int)p1[3]};
   };
-  // the 8 MFMAs of half s2; tile i + 1's operand is read while tile i's MFMA runs
-  auto mfma_half = [&](const uint8_t* A, int s2, const i32x8_t& bf) {
+  // the MFMAs of half s2 over the first NT row tiles (NT is a compile-time
+  // count, so the unrolled MFMA sequence stays free of branches); tile i + 1's
+  // operand is read while tile i's MFMA runs
+  auto mfma_half = [&](auto nt, const uint8_t* A, int s2, const i32x8_t& bf) {
+    constexpr int NT = decltype(nt)::value;
     i32x8_t an = load_a(A, s2, 0);
 #pragma unroll
-    for (int i = 0; i < MMI; i++) {
+    for (int i = 0; i < NT; i++) {
       const i32x8_t af = an;
-      if (i + 1 < MMI) an = load_a(A, s2, i + 1);
+      if (i + 1 < NT) an = load_a(A, s2, i + 1);
       acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, acc[i], 0, 0, 0, 127, 0, 127);
     }
   };
@@ -371,39 +410,53 @@ __global__ __launch_bounds__(512) void k_moe_gemm(const uint8_t* __restrict__ x8
   // barrier at the end of step k publishes group k + 2 and retires every read
   // of stage k % 3, which step k + 1 then refills with group k + 3.
   const int nk = (int)(K / MBK);
-  uint32_t sn = 0u, sn2 = 0u;                           // raw s8 of steps k + 1, k + 2
   issue(0, 0);
-  const uint32_t s0 = s8row[0];
-  if (nk > 1) {
-    issue(1, MBK);
-    sn = s8row[1];
-  }
+  if (nk > 1) issue(1, MBK);
+  load_s8_chunk(0);
   wait_vm<0>();
-  __syncthreads();                                      // also publishes rscale
-  Lut Lc = make_lut(s0);
+  __syncthreads();                                      // also publishes rscale and s8l
+  Lut Lc = make_lut(s8_of(0));
   i32x8_t bc, bn;
   lut_half(lds + MA_TILE, 0, Lc, bc);
 
-  int stage = 0;
-  for (int kt = 0; kt < nk; kt++) {
-    const int st1 = stage == 2 ? 0 : stage + 1;
-    const int st2 = st1 == 2 ? 0 : st1 + 1;
-    if (kt + 2 < nk) {
-      issue(st2, (int64_t)(kt + 2) * MBK);
-      sn2 = s8row[kt + 2];
+  // The last row tile of an expert is usually partial: the K loop runs the
+  // MFMAs of the first 2, 4, 6 or 8 row tiles (the fewest that cover the
+  // tile's rows), one instance of the loop per count.
+  auto k_loop = [&](auto nt, auto reload) {
+    int stage = 0;
+    for (int kt = 0; kt < nk; kt++) {
+      const int st1 = stage == 2 ? 0 : stage + 1;
+      const int st2 = st1 == 2 ? 0 : st1 + 1;
+      // K > MS8_CHUNK groups: the next chunk of s8 replaces the current one
+      // before step kt's look-ahead reads it (the last read of the current
+      // chunk was in step kt - 1, before its closing barrier)
+      if constexpr (decltype(reload)::value) {
+        if ((kt + 1) % MS8_CHUNK == 0 && kt + 1 < nk) {
+          load_s8_chunk(kt + 1);
+          __syncthreads();
+        }
+      }
+      if (kt + 2 < nk) issue(st2, (int64_t)(kt + 2) * MBK);
+      // (on the last step the second conversion reads a stale stage; unused)
+      const uint8_t* A = lds + stage * MSTAGE;
+      lut_half(A + MA_TILE, 1, Lc, bn);
+      mfma_half(nt, A, 0, bc);
+      Lc = make_lut(s8_of(kt + 1 < nk ? kt + 1 : kt));
+      lut_half(lds + st1 * MSTAGE + MA_TILE, 0, Lc, bc);
+      mfma_half(nt, A, 1, bn);
+      wait_vm<0>();
+      tile_barrier();
+      stage = st1;
     }
-    // (on the last step the second conversion reads a stale stage; unused)
-    const uint8_t* A = lds + stage * MSTAGE;
-    lut_half(A + MA_TILE, 1, Lc, bn);
-    mfma_half(A, 0, bc);
-    Lc = make_lut(sn);
-    lut_half(lds + st1 * MSTAGE + MA_TILE, 0, Lc, bc);
-    mfma_half(A, 1, bn);
-    wait_vm<0>();
-    tile_barrier();
-    sn = sn2;
-    stage = st1;
-  }
+  };
+  auto by_rows = [&](auto reload) {
+    if (ntile > 6) k_loop(std::integral_constant<int, 8>{}, reload);
+    else if (ntile > 4) k_loop(std::integral_constant<int, 6>{}, reload);
+    else if (ntile > 2) k_loop(std::integral_constant<int, 4>{}, reload);
+    else k_loop(std::integral_constant<int, 2>{}, reload);
+  };
+  if (G <= MS8_CHUNK) by_rows(std::false_type{});
+  else k_loop(std::integral_constant<int, MMI>{}, std::true_type{});   // K > 4096: every row tile
 
   // epilogue: C element r of a 32x32 tile sits at row 8*(r/4) + 4*h + r%4, col l32.
   // Stores go through a buffer range covering the tile's valid rows, so rows
@@ -415,6 +468,7 @@ __global__ __launch_bounds__(512) void k_moe_gemm(const uint8_t* __restrict__ x8
   const uint32_t cb = col < N ? (uint32_t)(col * 2) : 0x80000000u;   // columns past N: out of range
 #pragma unroll
   for (int i = 0; i < MMI; i++) {
+    if (i >= ntile) break;
 #pragma unroll
     for (int r = 0; r < 16; r++) {
       const int lr = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
