@@ -215,12 +215,13 @@ def test_gemm_ragged(W, kind, M, N, K):
     _check(W.wq_gemm(dev_bf16(xbits), *args, N), xbits, wdeq, chan)
 
 
-def test_prefill_full_size_all_rows(W):
-    # the prefill workload (8192 x 4096 . 14336 x 4096, MXFP4 per 32): every
-    # one of the 117 M outputs against the fp64 reference
+@pytest.mark.parametrize("kind", ["mxfp4", "int4"])
+def test_prefill_full_size_all_rows(W, kind):
+    # the prefill workload (8192 x 4096 . 14336 x 4096, MXFP4 per 32 or INT4
+    # per 128): every one of the 117 M outputs against the fp64 reference
     xbits, Wf = prefill_inputs(0)
-    args, wdeq, chan = _prep(W, "mxfp4", Wf)
-    banner("prefill full size mxfp4 8192x4096 . 14336x4096, all rows")
+    args, wdeq, chan = _prep(W, kind, Wf)
+    banner("prefill full size", kind, "8192x4096 . 14336x4096, all rows")
     y = W.wq_gemm(dev_bf16(xbits), *args, 14336)
     check_all_rows(y, xbits, wdeq, chan)
 
