@@ -1298,7 +1298,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_ring16(const uint16_t* __restr
 template <int WDT, int SPW, int WW, int CTW, int GSH>
 __global__ __launch_bounds__(64 * WW) __attribute__((amdgpu_waves_per_eu(WW / 4, WW / 4))) void k_gemv_wide(
     const uint16_t* __restrict__ x, int M, int64_t N, int64_t K, const uint8_t* __restrict__ w,
-    const void* __restrict__ sc, const float* __restrict__ chscale, float alpha, uint16_t* __restrict__ y) {
+    const void* __restrict__ sc, const float* __restrict__ chscale, float alpha, uint16_t* __restrict__ y, int cpw) {
   constexpr int EPL = WTraits<WDT>::bits == 4 ? 32 : 16;
   constexpr int KSTEP = 4 * EPL;
   constexpr int KSL = SPW * KSTEP;
@@ -1308,9 +1308,12 @@ __global__ __launch_bounds__(64 * WW) __attribute__((amdgpu_waves_per_eu(WW / 4,
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nl = lane & 15, g = lane >> 4;
-  const int64_t n0 = (int64_t)blockIdx.x * 16 * CTW;
+  // the workgroup's cpw columns (a multiple of 8, at most 16 CTW): the rows of
+  // its tiles past cpw lie outside the buffer ranges below and read as zeros
+  // without a memory access, and their outputs are not stored
+  const int64_t n0 = (int64_t)blockIdx.x * cpw;
   const uint32_t rowbytes = (uint32_t)(K * BPE2 / 2);
-  const int64_t nrows = N - n0 < 16 * CTW ? N - n0 : 16 * CTW;
+  const int64_t nrows = N - n0 < cpw ? N - n0 : cpw;
   constexpr int gs = gshift_of<WDT>(GSH);
   const uint32_t spr = (uint32_t)(K >> gs);
   constexpr int SB = scale_bytes<WDT>();
@@ -1422,7 +1425,7 @@ __global__ __launch_bounds__(64 * WW) __attribute__((amdgpu_waves_per_eu(WW / 4,
   for (int idx = threadIdx.x; idx < CTW * 256; idx += 64 * WW) {
     const int t = idx >> 8, m = (idx >> 4) & 15, n = idx & 15;
     const int64_t col = n0 + 16 * t + n;
-    if (m < M && col < N) {
+    if (m < M && col < N && 16 * t + n < cpw) {
       float v = 0.0f;
 #pragma unroll
       for (int wv = 0; wv < WW; wv++) v += red[((wv * CTW + t) * 16 + m) * 16 + n];
@@ -1508,9 +1511,20 @@ wq_status wide_go(int64_t M, const uint16_t* x, int64_t N, int64_t K, const uint
   // partials reuse it
   const size_t red = (size_t)WIDE_WW * WIDE_CTW * 1024, xb = (size_t)16 * K * 2;
   const size_t lds = xb > red ? xb : red;
-  const unsigned grid = (unsigned)((N + 16 * WIDE_CTW - 1) / (16 * WIDE_CTW));
+  // columns per workgroup: 16 CTW, or fewer (a multiple of 8) when that
+  // leaves CUs idle, so that the workgroups cover the CUs once (N = 14336:
+  // 256 workgroups of 56 columns instead of 224 of 64)
+  int ncu = 0;
+  if (cu_count(&ncu) != hipSuccess) return WQ_EHIP;
+  int64_t cpw = 16 * WIDE_CTW;
+  if ((N + cpw - 1) / cpw < ncu) {
+    const int64_t c = ((N + ncu - 1) / ncu + 7) / 8 * 8;
+    cpw = c < 8 ? 8 : (c > cpw ? cpw : c);
+  }
+  const unsigned grid = (unsigned)((N + cpw - 1) / cpw);
   if (allow_lds<k_gemv_wide<WDT, SPW, WIDE_WW, WIDE_CTW, GSH>>(lds) != hipSuccess) return WQ_EHIP;
-  k_gemv_wide<WDT, SPW, WIDE_WW, WIDE_CTW, GSH><<<grid, 64 * WIDE_WW, lds, s>>>(x, (int)M, N, K, w, sc, ch, alpha, y);
+  k_gemv_wide<WDT, SPW, WIDE_WW, WIDE_CTW, GSH><<<grid, 64 * WIDE_WW, lds, s>>>(x, (int)M, N, K, w, sc, ch, alpha, y,
+                                                                              (int)cpw);
   return WQ_OK;
 }
 
