@@ -22,6 +22,55 @@ def test_routing_topk_bruteforce_and_ties():
     assert list(ids[0]) == [1, 4, 0, 2]
 
 
+def test_routing_weights_closed_forms():
+    # logits ln(1), ln(2), ..., ln(E): the softmax is (e + 1) / (E (E + 1) / 2)
+    E, k = 64, 8
+    z = np.log(np.arange(1, E + 1, dtype=np.float64)).astype(np.float32)[None, :]
+    ids, w = W.route_topk(z, k)
+    assert list(ids[0]) == list(range(E - 1, E - 1 - k, -1))
+    expect = (np.arange(E, E - k, -1) / (E * (E + 1) / 2)).astype(np.float64)
+    assert np.allclose(w[0], expect, rtol=2e-6, atol=0)
+    # two experts: logits (a, 0) give sigmoid(a) and 1 - sigmoid(a)
+    a = np.float32(1.25)
+    ids, w = W.route_topk(np.array([[a, 0.0]], np.float32), 2)
+    sig = 1.0 / (1.0 + np.exp(-1.25))
+    assert list(ids[0]) == [0, 1] and abs(w[0, 0] - sig) < 1e-7 and abs(w[0, 1] - (1 - sig)) < 1e-7
+    # equal logits: every probability 1 / E, ids in increasing order
+    ids, w = W.route_topk(np.full((1, 16), 3.5, np.float32), 4)
+    assert list(ids[0]) == [0, 1, 2, 3] and np.all(w[0] == np.float32(1 / 16))
+    # a constant added to every logit changes nothing
+    g = np.random.default_rng(7)
+    z = g.standard_normal((8, 64)).astype(np.float32) * 0.5
+    i0, w0 = W.route_topk(z, 8)
+    i1, w1 = W.route_topk(z + np.float32(4.0), 8)
+    assert np.array_equal(i0, i1) and np.allclose(w0, w1, rtol=1e-6)
+
+
+def test_channel_scale_closed_forms():
+    # channels whose largest group scale is 448 * 2^j: ch = 8 * 2^j exactly and
+    # that group's fp8 scale is 56 exactly; the other groups' codes round
+    # s / ch to the nearest E4M3 value
+    js = np.arange(-6, 3)
+    smax = 448.0 * np.exp2(js)
+    others = np.array([1.0, 3.0, 0.5, 100.0]) * np.exp2(js)[:, None]
+    s = np.concatenate([smax[:, None], others], axis=1).astype(np.float32)
+    bits = to_bf16_bits(s)
+    assert np.array_equal(bf16_decode(bits), s)                   # every value exact in bf16
+    s8, ch = W.scale_recipe(bits)
+    assert np.array_equal(ch, (8.0 * np.exp2(js)).astype(np.float32))
+    assert np.all(e4m3_decode(s8[:, 0]) == 56.0)
+    ratio = others / (8.0 * np.exp2(js))[:, None]                 # exact: powers of two
+    assert np.array_equal(s8[:, 1:], e4m3_from_f32(ratio.astype(np.float32)))
+    # any channel: ch / 8 is the float nearest amax / 448 (checked in fp64)
+    g = np.random.default_rng(3)
+    sb = to_bf16_bits(np.abs(g.standard_normal((200, 16))).astype(np.float32) * 0.01)
+    _, ch = W.scale_recipe(sb)
+    amax = bf16_decode(sb).max(axis=1).astype(np.float64) / 448.0
+    c8 = ch.astype(np.float64) / 8.0
+    ulp = np.spacing(np.abs(c8).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(c8 - amax) <= ulp / 2)
+
+
 def test_grouping_is_stable_and_complete():
     z = moe_router_logits(1, 300, 16)
     ids, _ = W.route_topk(z, 4)
@@ -43,9 +92,7 @@ def test_scale_recipe_range_and_lut_no_clip():
     # the largest group scale of each channel maps to 448/8 = 56
     assert np.all(v.max(axis=1) == 56.0)
     assert np.all(v > 0)
-    # channel scale is 8 * RN_f32(amax/448)
-    amax = bf16_decode(sb).max(axis=1).astype(np.float32)
-    assert np.array_equal(ch, np.float32(8) * (amax / np.float32(448)))
+    # (the channel scale itself: test_channel_scale_closed_forms)
     table = W.lut(s8)
     tv = e4m3_decode(table)
     # |w * s8| <= 8 * 56 = 448: no entry saturates, every entry is the rounded product
