@@ -109,8 +109,10 @@ class Region:
     region's launches while the device is still busy and the submission
     latency stays off the clock: event a fires when the busy kernel ends, and
     the first launch follows at once.  The busy kernel's iteration count is
-    sized from a measured rate to last about four times the host's submission
-    time.
+    sized from a measured rate to last about eight times the host's submission
+    time (at least 0.3 ms): the submission time of one region varies with the
+    host's load, and a region whose launches are still being submitted when
+    the busy kernel ends is timed partly on the host.
     `rounds` regions are timed; ms per launch is their median.  A one-wave
     clock probe (wq_util_clock) runs just before event a and just after event
     b and records the shader clock at each end of every region."""
@@ -128,7 +130,7 @@ class Region:
         enqueue()                                   # untimed pass: host submission time
         self.host_ms = (time.perf_counter() - t) * 1e3
         torch.cuda.synchronize()
-        self.iters = int(min(max(4.0 * max(self.host_ms, 0.05) / self.ms_per_iter, 1000), 1 << 24))
+        self.iters = int(min(max(max(8.0 * self.host_ms, 0.3) / self.ms_per_iter, 1000), 1 << 24))
         self.windows = []
         self.clk = torch.zeros((rounds, 2, 2), dtype=torch.int64, device="cuda")
         self.wall_khz = W.wq_util_wall_clock_khz()
