@@ -357,11 +357,13 @@ def test_gemv_x_through_lds(W, kind, M, N, K):
 
 @pytest.mark.parametrize("kind", ["int4", "mxfp4", "e4m3"])
 @pytest.mark.parametrize("M", [5, 16])
-@pytest.mark.parametrize("N,K", [(4200, 2048), (4136, 4096)])
+@pytest.mark.parametrize("N,K", [(4200, 2048), (4136, 4096), (9000, 4096), (16400, 2048)])
 def test_gemv_x_once_per_workgroup(W, kind, M, N, K):
-    # 5 <= M <= 16, more 16-column tiles than CUs, K = 2048 or 4096: 64 columns
-    # per 16-wave workgroup with x staged once in LDS (ragged last workgroups
-    # of 40 and 40 columns)
+    # 5 <= M <= 16, more 16-column tiles than CUs, K = 2048 or 4096: x staged
+    # once in LDS per 16-wave workgroup of up to 64 columns, as few as cover N
+    # with one workgroup per CU (256 CUs: 24 columns at N = 4200 and 4136,
+    # last workgroups of 24 and 8 columns; 40 at N = 9000, the last one whole;
+    # 64 at N = 16400, a last workgroup of 16 columns)
     g = np.random.default_rng(950 + M * 3 + N + K)
     Wf = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
     Wf[:, g.choice(K, 5, replace=False)] *= 30
