@@ -271,8 +271,8 @@ def time_eager(torch, fn, reps, warm=3, rounds=3):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("wq_gemm.hip", "wq_device.h", "wq_quant.hip"):
-        with open(os.path.join(ROOT, "weight_only_quantized_quant_amd", "csrc", f), "rb") as fh:
+    for f in ("csrc/wq_gemm.hip", "csrc/wq_device.h", "csrc/wq_quant.hip", "build.py"):
+        with open(os.path.join(ROOT, "weight_only_quantized_quant_amd", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 

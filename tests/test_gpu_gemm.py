@@ -84,6 +84,33 @@ def test_gemv_tile_rounds(W, kind, M, N, K):
     _check(y, xbits, wdeq, chan)
 
 
+@pytest.mark.parametrize("kind,group,M,N,K", [
+    ("int4", 128, 1, 8190, 2048),     # 512 tiles (2 per CU on 256 CUs), the last with 14 rows
+    ("int4", 128, 3, 9001, 4096),     # 563 tiles: the last 51 become 102 tiles of 8 rows
+    ("int4", 32, 4, 8200, 4096),      # 513 tiles: the last in two 8-row halves, the second empty
+    ("int4", 64, 2, 16400, 8192),     # 16 steps per wave slice
+    ("mxfp4", 32, 4, 14335, 4096),    # the decode workload's shape less one row
+    ("int4", 128, 4, 8200, 14336),    # 28 steps per wave slice with x through the ring slots
+    ("int4", 128, 2, 4097, 4096),     # 257 tiles, the last one with 1 row
+    ("int4", 32, 1, 3205, 8192),
+    ("int4", 64, 2, 17, 4096),        # one full tile of 16 rows and one of 1
+    ("mxfp4", 32, 2, 4105, 8192),
+    ("mxfp4", 32, 1, 14336, 4096),
+])
+def test_gemv_more_shapes(W, kind, group, M, N, K):
+    # N from 17 to 16400 with ragged last tiles and balancing rounds of 8-row
+    # tiles, K from 2048 to 14336, scale groups 32 to 128, M = 1-4
+    g = np.random.default_rng(M * 11 + N + K + group)
+    Wf = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
+    Wf[:, g.choice(K, 3, replace=False)] *= 40
+    Wf[-2:] *= 30                                                # the ragged last tile
+    xbits = to_bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    args, wdeq, chan = _prep(W, kind, Wf, group)
+    del Wf
+    banner("gemv more shapes", kind, group, M, N, K)
+    _check(W.wq_gemm(dev_bf16(xbits), *args, N), xbits, wdeq, chan)
+
+
 @pytest.mark.parametrize("group", [32, 64])
 def test_gemv_int4_small_groups(W, group):
     g = np.random.default_rng(group)

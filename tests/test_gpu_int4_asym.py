@@ -125,6 +125,20 @@ def test_gemm_ragged(W, group, M, N, K):
     _check(W.wq_gemm(dev_bf16(xbits), *args, N), xbits, wdeq)
 
 
+@pytest.mark.parametrize("group,M,N,K", [(32, 3, 9001, 4096), (128, 4, 8200, 2048), (32, 2, 4795, 4096),
+                                         (128, 1, 3205, 8192)])
+def test_gemv_more_shapes(W, group, M, N, K):
+    # ragged last tiles and balancing rounds of 8-row tiles, K 2048 to 8192,
+    # groups of 32 (128 scale-zero words per row at K = 4096) and 128
+    r = np.random.default_rng(M * 3 + N + K + group)
+    Wf = (r.standard_normal((N, K)) * 0.02 + 0.01 * r.standard_normal((N, 1))).astype(np.float32)
+    Wf[:, r.choice(K, 3, replace=False)] *= 40
+    xbits = to_bf16_bits(r.standard_normal((M, K)).astype(np.float32))
+    args, wdeq = _args(W, Wf, group)
+    banner("gemv more shapes asymmetric int4", group, M, N, K)
+    _check(W.wq_gemm(dev_bf16(xbits), *args, N), xbits, wdeq)
+
+
 @pytest.fixture(scope="module")
 def decode_asym(W):
     _, Wf = decode_inputs(1, 0)

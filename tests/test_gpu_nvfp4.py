@@ -137,6 +137,19 @@ def test_gemm_ragged(W, M, N, K):
     _check(W.wq_gemm(dev_bf16(xbits), *args, N, alpha=g), xbits, wdeq, g)
 
 
+@pytest.mark.parametrize("M,N,K", [(3, 9001, 4096), (1, 8200, 2048), (1, 4795, 4096), (2, 3205, 8192)])
+def test_gemv_more_shapes(W, M, N, K):
+    # ragged last tiles and balancing rounds of 8-row tiles, K 2048 to 8192
+    r = np.random.default_rng(M * 13 + N + K)
+    Wf = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
+    Wf[:, r.choice(K, 3, replace=False)] *= 40
+    xbits = to_bf16_bits(r.standard_normal((M, K)).astype(np.float32))
+    g = tensor_scale(Wf)
+    args, wdeq = _nv_args(W, Wf, g)
+    banner("gemv more shapes nvfp4", M, N, K, g)
+    _check(W.wq_gemm(dev_bf16(xbits), *args, N, alpha=g), xbits, wdeq, g)
+
+
 def test_gemm_alpha_one_and_unit_scales(W):
     # g = 1 with every block scale 1.0: y = x . e2m1 values exactly representable
     K, N, M = 512, 64, 3
