@@ -411,3 +411,32 @@ def test_gemv_long_k(W, kind, M, N):
     args, wdeq, chan = _prep(W, kind, Wf)
     banner("gemv long K", kind, M, N, K)
     _check(W.wq_gemm(dev_bf16(xbits), *args, N), xbits, wdeq, chan)
+
+
+def _random_cases(n, seed=2024):
+    """Seeded random shapes over every dispatch range: M from 1 to 300 (the
+    decode forms, launches of 32 rows and the prefill tiles), N from 1 to
+    5000, K a multiple of 128 up to 5120, each format and INT4 group."""
+    g = np.random.default_rng(seed)
+    kinds = [("int4", 128), ("int4", 64), ("int4", 32), ("mxfp4", 32), ("e4m3", 0)]
+    out = []
+    while len(out) < n:
+        M = int(np.exp(g.uniform(0, np.log(300))))
+        N = int(g.integers(1, 5001))
+        K = 128 * int(g.integers(1, 41))
+        kind, group = kinds[len(out) % len(kinds)]
+        if M * N * K > 1.5e9:
+            continue
+        out.append((kind, group, M, N, K, int(g.integers(1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("kind,group,M,N,K,seed", _random_cases(60))
+def test_gemm_random_shapes(W, kind, group, M, N, K, seed):
+    g = np.random.default_rng(seed)
+    Wf = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
+    Wf[:, g.choice(K, min(3, K), replace=False)] *= 40
+    xbits = to_bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    args, wdeq, chan = _prep(W, kind, Wf, group or 128)
+    banner("gemm random shape", kind, group, M, N, K, seed)
+    _check(W.wq_gemm(dev_bf16(xbits), *args, N), xbits, wdeq, chan)

@@ -176,3 +176,29 @@ def test_zero_point_shifts_the_result(W):
         y = W.wq_gemm(dev_bf16(xbits[:M]), *args, 200)
         _check(y, xbits[:M], wdeq)
         assert np.all(bf16_decode(host_bits16(y))[:, ::9] == 0.0)
+
+
+def _random_cases(n, seed=2026):
+    """Seeded random shapes: M 1-300, N 1-5000, K a multiple of 128 up to 5120,
+    groups 32, 64 and 128 in turn."""
+    g = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        M = int(np.exp(g.uniform(0, np.log(300))))
+        N = int(g.integers(1, 5001))
+        K = 128 * int(g.integers(1, 41))
+        if M * N * K > 1.5e9:
+            continue
+        out.append(((32, 64, 128)[len(out) % 3], M, N, K, int(g.integers(1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("group,M,N,K,seed", _random_cases(15))
+def test_gemm_random_shapes(W, group, M, N, K, seed):
+    r = np.random.default_rng(seed)
+    Wf = (r.standard_normal((N, K)) * 0.02 + 0.01 * r.standard_normal((N, 1))).astype(np.float32)
+    Wf[:, r.choice(K, 3, replace=False)] *= 40
+    xbits = to_bf16_bits(r.standard_normal((M, K)).astype(np.float32))
+    args, wdeq = _args(W, Wf, group)
+    banner("gemm random shape asymmetric int4", group, M, N, K, seed)
+    _check(W.wq_gemm(dev_bf16(xbits), *args, N), xbits, wdeq)

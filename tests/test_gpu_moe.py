@@ -203,6 +203,23 @@ def test_moe_gemm_small(W, T, E, k, K, N):
     _small_case(W, T, E, k, K, N, seed=T + E + k + K + N)
 
 
+def _random_moe_cases(n, seed=2027):
+    """Seeded random configurations: 1-800 tokens, 1-16 experts, top-k 1-4,
+    K a multiple of 128 up to 2560, N 1-600, gathered or already grouped rows."""
+    g = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        E = int(g.integers(1, 17))
+        out.append((int(g.integers(1, 801)), E, int(g.integers(1, min(E, 4) + 1)), 128 * int(g.integers(1, 21)),
+                    int(g.integers(1, 601)), bool(g.integers(0, 2)), int(g.integers(1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("T,E,k,K,N,identity,seed", _random_moe_cases(12))
+def test_moe_gemm_random(W, T, E, k, K, N, identity, seed):
+    _small_case(W, T, E, k, K, N, seed=seed, identity=identity)
+
+
 def test_moe_gemm_subnormal_group_scales(W):
     # Groups whose INT4 scale sits ~10^4 below the channel's largest: their
     # fp8 scale (56 * s / max s) lands in the E4M3 subnormal range and so do

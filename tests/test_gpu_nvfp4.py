@@ -207,3 +207,29 @@ def test_alpha_scales_the_output(W):
         _check(W.wq_gemm(dev_bf16(xb), *args, 272, alpha=-0.3), xb, wdeq, -0.3)
     with pytest.raises(ValueError):
         W.wq_gemm(dev_bf16(xbits), *args, 272, alpha=float("nan"))
+
+
+def _random_cases(n, seed=2025):
+    """Seeded random shapes: M 1-300, N 1-5000, K a multiple of 128 up to 5120."""
+    g = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        M = int(np.exp(g.uniform(0, np.log(300))))
+        N = int(g.integers(1, 5001))
+        K = 128 * int(g.integers(1, 41))
+        if M * N * K > 1.5e9:
+            continue
+        out.append((M, N, K, int(g.integers(1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K,seed", _random_cases(16))
+def test_gemm_random_shapes(W, M, N, K, seed):
+    r = np.random.default_rng(seed)
+    Wf = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
+    Wf[:, r.choice(K, 3, replace=False)] *= 40
+    xbits = to_bf16_bits(r.standard_normal((M, K)).astype(np.float32))
+    g = tensor_scale(Wf)
+    args, wdeq = _nv_args(W, Wf, g)
+    banner("gemm random shape nvfp4", M, N, K, seed)
+    _check(W.wq_gemm(dev_bf16(xbits), *args, N, alpha=g), xbits, wdeq, g)

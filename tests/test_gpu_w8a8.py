@@ -126,6 +126,27 @@ def test_gemm_ragged(W, a_mode, b_mode, M, N, K):
     _check(_run(W, ac, a_args, bc, b_args), ac, a_full, bc, b_full)
 
 
+def _random_w8a8_cases(n, seed=2028):
+    """Seeded random shapes (M 1-600, N 3-3000, K a multiple of 128 up to
+    4096) and scale layouts."""
+    g = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        M, N, K = int(g.integers(1, 601)), int(g.integers(3, 3001)), 128 * int(g.integers(1, 33))
+        if M * N * K > 1.5e9:
+            continue
+        a_mode, b_mode = MODES[len(out) % len(MODES)]
+        out.append((a_mode, b_mode, M, N, K, int(g.integers(1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("a_mode,b_mode,M,N,K,seed", _random_w8a8_cases(15))
+def test_gemm_random_shapes(W, a_mode, b_mode, M, N, K, seed):
+    ac, a_args, a_full, bc, b_args, b_full = _operands(M, N, K, seed, a_mode, b_mode)
+    banner("w8a8 random shape", a_mode, b_mode, M, N, K, seed)
+    _check(_run(W, ac, a_args, bc, b_args), ac, a_full, bc, b_full)
+
+
 def test_gemm_exact_small_integers(W):
     # unit scales and small E4M3 integers: every partial sum is exact in fp32,
     # so y is the single bf16 rounding of the exact product
