@@ -202,3 +202,23 @@ def test_gemm_random_shapes(W, group, M, N, K, seed):
     args, wdeq = _args(W, Wf, group)
     banner("gemm random shape asymmetric int4", group, M, N, K, seed)
     _check(W.wq_gemm(dev_bf16(xbits), *args, N), xbits, wdeq)
+
+
+def _random_quant_cases(n, seed=2031):
+    """Seeded random shapes: 4-300 rows, 128-4096 columns in steps of 128,
+    groups 32 to 128, shifted distributions."""
+    g = np.random.default_rng(seed)
+    return [((32, 64, 128)[i % 3], int(g.integers(4, 301)), 128 * int(g.integers(1, 33)), bool(i % 2),
+             float(g.uniform(-0.8, 0.8)), int(g.integers(1 << 30))) for i in range(n)]
+
+
+@pytest.mark.parametrize("group,rows,cols,bf16,shift,seed", _random_quant_cases(9))
+def test_quantize_random_shapes(W, group, rows, cols, bf16, shift, seed):
+    a = _wide(rows, cols, seed, shift)
+    if bf16:
+        bits = to_bf16_bits(a)
+        x, ref_in = dev_bf16(bits), bf16_bits_to_f32(bits)
+    else:
+        x, ref_in = dev_f32(a), a
+    banner("asymmetric int4 quantize random shape", group, rows, cols, "bf16" if bf16 else "fp32", shift)
+    _quant_check(W, x, ref_in, group)

@@ -233,3 +233,23 @@ def test_gemm_random_shapes(W, M, N, K, seed):
     args, wdeq = _nv_args(W, Wf, g)
     banner("gemm random shape nvfp4", M, N, K, seed)
     _check(W.wq_gemm(dev_bf16(xbits), *args, N, alpha=g), xbits, wdeq, g)
+
+
+def _random_quant_cases(n, seed=2030):
+    """Seeded random shapes: 3-300 rows, 32-2048 columns in steps of 16."""
+    g = np.random.default_rng(seed)
+    return [(int(g.integers(3, 301)), 16 * int(g.integers(2, 129)), bool(i % 2), int(g.integers(1 << 30)))
+            for i in range(n)]
+
+
+@pytest.mark.parametrize("rows,cols,bf16,seed", _random_quant_cases(8))
+def test_quantize_random_shapes(W, rows, cols, bf16, seed):
+    # seeded random shapes, wide values: codes and scales bit for bit
+    a = _wide(rows, cols, seed)
+    if bf16:
+        bits = to_bf16_bits(a)
+        x, ref_in = dev_bf16(bits), bf16_bits_to_f32(bits)
+    else:
+        x, ref_in = dev_f32(a), a
+    banner("nvfp4 quantize random shape", rows, cols, "bf16" if bf16 else "fp32")
+    _quant_check(W, x, ref_in, tensor_scale(ref_in))

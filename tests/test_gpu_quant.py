@@ -249,3 +249,45 @@ def test_dequant_int4_every_code_and_scale(W):
         pk = OI.pack_int4(qq)
         out = W.wq_dequant(dev_words(pk), W.WQ_INT4X8, dev_bf16(ss), W.WQ_BF16, group, 64, 512)
         assert np.array_equal(host_bits16(out), OD.dequant_int4(pk, ss, group))
+
+
+# ---------------------------------------------------------------------------
+# seeded random shapes: every quantizer, codes and scales bit for bit
+# ---------------------------------------------------------------------------
+def _random_quant_cases(n, seed=2029):
+    g = np.random.default_rng(seed)
+    kinds = [("e4m3", 16), ("e4m3", 64), ("e4m3", 128), ("e4m3", 256), ("e4m3", -1),
+             ("mxfp4", 16), ("mxfp4", 32), ("int4", 32), ("int4", 64), ("int4", 128)]
+    out = []
+    for i in range(n):
+        kind, block = kinds[i % len(kinds)]
+        unit = 128 if block == -1 else 32 if kind == "mxfp4" else block      # MXFP4: cols % 32 (either block)
+        out.append((kind, block, int(g.integers(1, 301)), unit * int(g.integers(1, 65)), bool(i % 2),
+                    int(g.integers(1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("kind,block,rows,cols,bf16,seed", _random_quant_cases(30))
+def test_quantizers_random_shapes(W, kind, block, rows, cols, bf16, seed):
+    a = _wide((rows, cols), seed=seed, zero_blocks=2, block=128 if block == -1 else block)
+    if bf16:
+        bits = to_bf16_bits(a)
+        x, ref_in = dev_bf16(bits), bf16_bits_to_f32(bits)
+    else:
+        x, ref_in = dev_f32(a), a
+    banner("quantizer random shape", kind, block, rows, cols, "bf16" if bf16 else "fp32")
+    if kind == "e4m3":
+        codes, scales = W.quantize_e4m3(x, block)
+        wc, ws = OE.quantize_e4m3(ref_in, block)
+        assert np.array_equal(host_f32(scales).view(np.uint32), ws.view(np.uint32))
+        assert np.array_equal(host_u8(codes), wc)
+    elif kind == "mxfp4":
+        codes, scales = W.quantize_mxfp4(x, block)
+        wc, ws = OM.quantize_mxfp4(ref_in, block)
+        assert np.array_equal(host_u8(scales), ws)
+        assert np.array_equal(host_u8(codes), wc)
+    else:
+        packed, scales = W.quantize_int4(x, block)
+        wp, ws, _ = OI.quantize_int4(ref_in, block)
+        assert np.array_equal(host_bits16(scales), ws)
+        assert np.array_equal(host_words(packed), wp)
