@@ -9,8 +9,10 @@ bf16 activations and output -- the decode W4A16 workload.  The weights are
 quantized on the GPU by quantize_int4 and replicated into 24 resident copies
 (727 MB) that the steps cycle through, so that the 256 MB Infinity Cache
 cannot serve them: every step streams its weights from HBM.  The K timed
-steps are launched as one HIP graph replay, bracketed by device
-synchronisation; `value` is algorithmic bytes / time.
+steps are launched as one HIP graph replay behind a bounded busy kernel (so
+that the host's submission stays off the clock; see Region), in --rounds
+rounds; ms per step is the median round and `value` is algorithmic bytes /
+that time.
 
 The same JSON line carries the roofline of that kernel (HIP events over the
 timed region on the launch stream), the oracle timed on the host (`cpu_baseline`)
@@ -28,7 +30,7 @@ out where sysfs does not expose them).
 
 --only CASE runs a single case without the full summary (for rocprofv3):
 decode (the same graph-timed steps as the headline, prints one short JSON
-line), decode_m1 (the headline's launches, eager, for counter runs), decode_m4, decode_m16, decode_w8, decode_nvfp4, decode_asym, prefill, prefill_nvfp4, w8a8_block, w8a8_channel, quant_e4m3, quant_mxfp4, quant_mxfp8, wquant_mxfp4, copy,
+line), decode_m1 (the headline's launches, eager, for counter runs), decode_m4, decode_m16, decode_w8, decode_nvfp4, decode_asym, prefill, prefill_nvfp4, prefill_int4, w8a8_block, w8a8_channel, quant_e4m3, quant_mxfp4, quant_mxfp8, wquant_mxfp4, copy,
 moe_gate_up, moe_down, stream_decode (the read-only stream of the decode weight
 copies), stream_2g, torch_matmul (hipBLASLt on the dequantized prefill weights).
 """
