@@ -1,0 +1,108 @@
+"""Captured HIP-graph replays of the library's launches (the form the decode
+benchmark times) reproduce the eager results bit for bit, on every replay,
+with eager launches and host synchronisation between the replays.  The eager
+results themselves are checked against the oracle by the other GPU tests;
+here only replay == eager is asserted (both run the same kernels on the same
+inputs, and every kernel is deterministic)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import e4m3 as OE
+from oracle import int4 as OI
+from oracle import mxfp4 as OM
+from synthetic import decode_inputs, prefill_inputs
+from tests.gpu_helpers import banner, dev_bf16, dev_f32, dev_u8, dev_words
+
+pytestmark = pytest.mark.gpu
+
+REPLAYS = 3
+
+
+@pytest.fixture(scope="module")
+def W():
+    import weight_only_quantized_quant_amd as W
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return W
+
+
+def _weights(W, kind, Wf):
+    """Device weight arguments of wq_gemm, quantized by the oracle."""
+    if kind == "int4":
+        packed, sb, _ = OI.quantize_int4(Wf, 128)
+        return dev_words(packed), W.WQ_INT4X8, dev_bf16(sb), W.WQ_BF16, 128
+    if kind == "mxfp4":
+        codes, sc = OM.quantize_mxfp4(Wf, 32)
+        return dev_u8(codes), W.WQ_E2M1X2, dev_u8(sc), W.WQ_E8M0, 32
+    codes, s = OE.quantize_e4m3(Wf, -1)
+    return dev_u8(codes), W.WQ_E4M3, dev_f32(s[:, 0]), W.WQ_F32, Wf.shape[1]
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype in (torch.bfloat16, torch.float16) else t.view(torch.uint8)
+
+
+def _replay_matches(fill, eager_fn, capture_fn, outs, refs, interleave):
+    """Capture capture_fn (writing outs), replay it REPLAYS times with outs
+    overwritten, interleave() run eagerly and the host synchronised before
+    each replay, and compare every replay with refs bit for bit."""
+    eager_fn()                                   # warm: attributes set outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        capture_fn()
+    for r in range(REPLAYS):
+        for o in outs:
+            o.view(torch.uint8).fill_(fill + r)
+        interleave()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, ref in zip(outs, refs):
+            assert torch.equal(_bits(o), _bits(ref)), f"replay {r} differs from the eager result"
+
+
+@pytest.mark.parametrize("kind,M,N,K", [
+    ("int4", 1, 14336, 4096),      # split-K ring
+    ("int4", 4, 4105, 4096),       # ring with x in the slots, ragged N
+    ("int4", 16, 14336, 4096),     # x-once workgroups
+    ("e4m3", 1, 4096, 4096),       # weights straight into registers
+    ("mxfp4", 3, 1000, 2048),      # ring, 3 tokens
+    ("int4", 300, 520, 512),       # prefill GEMM, ragged tiles
+    ("mxfp4", 40, 700, 1024),      # 17-64 rows: grouped decode launches
+])
+def test_gemm_graph_replays(W, kind, M, N, K):
+    banner("graph replay wq_gemm", kind, M, N, K)
+    if M <= 16:
+        xbits, Wf = decode_inputs(M, K=K, N=N, seed=11)
+    else:
+        xbits, Wf = prefill_inputs(seed=11, M=M, K=K, N=N)
+    x = dev_bf16(xbits)
+    wq, wdt, sc, sdt, group = _weights(W, kind, Wf)
+    ref = W.wq_gemm(x, wq, wdt, sc, sdt, group, N)
+    torch.cuda.synchronize()
+    y = torch.empty_like(ref)
+    other = torch.empty_like(ref)
+    _replay_matches(
+        0x11,
+        lambda: W.wq_gemm(x, wq, wdt, sc, sdt, group, N, y=y),
+        lambda: W.wq_gemm(x, wq, wdt, sc, sdt, group, N, y=y),
+        [y], [ref],
+        lambda: W.wq_gemm(x, wq, wdt, sc, sdt, group, N, y=other))
+
+
+def test_quantizer_graph_replays(W):
+    banner("graph replay quantizers 300 x 512")
+    rng = np.random.default_rng(5)
+    a = torch.from_numpy(rng.standard_normal((300, 512)).astype(np.float32)).cuda().to(torch.bfloat16)
+    c4, s4 = W.quantize_mxfp4(a, 32)
+    c8, s8 = W.quantize_e4m3(a, 128)
+    torch.cuda.synchronize()
+    oc4, os4, oc8, os8 = (torch.empty_like(t) for t in (c4, s4, c8, s8))
+
+    def run():
+        W.quantize_mxfp4(a, 32, codes=oc4, scales=os4)
+        W.quantize_e4m3(a, 128, codes=oc8, scales=os8)
+
+    _replay_matches(0x5A, run, run, [oc4, os4, oc8, os8], [c4, s4, c8, s8],
+                    lambda: W.quantize_e4m3(a, -1))
