@@ -11,7 +11,9 @@ import torch
 from oracle import e4m3 as OE
 from oracle import int4 as OI
 from oracle import mxfp4 as OM
-from synthetic import decode_inputs, prefill_inputs
+from oracle import w4a8 as OW
+from oracle import w8a8 as O8
+from synthetic import decode_inputs, prefill_inputs, to_bf16_bits
 from tests.gpu_helpers import banner, dev_bf16, dev_f32, dev_u8, dev_words
 
 pytestmark = pytest.mark.gpu
@@ -106,3 +108,48 @@ def test_quantizer_graph_replays(W):
 
     _replay_matches(0x5A, run, run, [oc4, os4, oc8, os8], [c4, s4, c8, s8],
                     lambda: W.quantize_e4m3(a, -1))
+
+
+def test_w8a8_graph_replays(W):
+    banner("graph replay wq_gemm_w8a8 300 x 520 x 512, 1x128 x 128x128 scales")
+    g = np.random.default_rng(3)
+    M, N, K = 300, 520, 512
+    kb = K // 128
+    ac, sa = OE.quantize_e4m3(g.standard_normal((M, K)).astype(np.float32), 128)
+    bc, sb = O8.quantize_e4m3_block2d((g.standard_normal((N, K)) * 0.02).astype(np.float32))
+    a, a_s, b, b_s = dev_u8(ac), dev_f32(sa), dev_u8(bc), dev_f32(sb)
+    ref = W.wq_gemm_w8a8(a, a_s, kb, 1, b, b_s, kb, 1, 128)
+    torch.cuda.synchronize()
+    y, other = torch.empty_like(ref), torch.empty_like(ref)
+    run = lambda: W.wq_gemm_w8a8(a, a_s, kb, 1, b, b_s, kb, 1, 128, y=y)
+    _replay_matches(0x33, run, run, [y], [ref], lambda: W.wq_gemm_w8a8(a, a_s, kb, 1, b, b_s, kb, 1, 128, y=other))
+
+
+def test_moe_graph_replays(W):
+    """Routing, grouping and the grouped W4A8 GEMM in one graph: the offsets
+    and row map stay on the device between the launches."""
+    banner("graph replay moe route + w4a8 gemm: T 64, E 8, k 2, K 512, N 256")
+    g = np.random.default_rng(4)
+    T, E, k, K, N = 64, 8, 2, 512, 256
+    logits = torch.from_numpy(g.standard_normal((T, E)).astype(np.float32)).cuda()
+    x8, a_s = OW.quantize_tokens(to_bf16_bits(g.standard_normal((T, K)).astype(np.float32)))
+    x8d, a_sd = dev_u8(x8), dev_f32(a_s)
+    packed, sbits = [], []
+    for _ in range(E):
+        p, sb, _ = OI.quantize_int4((g.standard_normal((N, K)) * 0.02).astype(np.float32), 128)
+        packed.append(p)
+        sbits.append(sb)
+    wq2, s8d, chd = W.wq_w4a8_prepack(dev_words(np.stack(packed)), dev_bf16(np.stack(sbits)))
+    ids_r, _, off_r, rt_r, _ = W.wq_moe_route(logits, k)
+    ref = W.wq_moe_gemm_w4a8(x8d, a_sd, rt_r, off_r, wq2, s8d, chd)
+    torch.cuda.synchronize()
+    y = torch.empty_like(ref)
+    held = {}
+
+    def run():
+        ids, _, off, rt, _ = W.wq_moe_route(logits, k)
+        held.update(ids=ids, off=off)
+        W.wq_moe_gemm_w4a8(x8d, a_sd, rt, off, wq2, s8d, chd, y=y)
+
+    _replay_matches(0x44, run, run, [y], [ref], lambda: W.wq_moe_route(logits, k))
+    assert torch.equal(held["ids"], ids_r) and torch.equal(held["off"], off_r)
