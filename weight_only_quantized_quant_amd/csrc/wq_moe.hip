@@ -45,81 +45,133 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 // ---------------------------------------------------------------------------
 // Routing and grouping
 // ---------------------------------------------------------------------------
+// One wave per token, lane e holding logit e (E <= 64).  The softmax maximum
+// and sum are xor butterflies over the wave.  The top k follow from each
+// expert's rank: the number of experts with a larger logit plus those with an
+// equal logit and a lower id (the order of the oracle's stable sort), counted
+// by every lane against the token's logits staged in the wave's own LDS row
+// (read as broadcasts).  The lanes ranked below k write themselves to
+// position rank.  Lanes past E hold -inf, which no finite logit ranks below.
 __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, int64_t T, int E, int k,
                                                int32_t* __restrict__ ids, float* __restrict__ wts) {
-  const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;                                   // whole wave
+  __shared__ __attribute__((aligned(16))) float zs[4][64];
+  const int lane = threadIdx.x & 63, wl = threadIdx.x >> 6;
+  const int64_t t = (int64_t)blockIdx.x * 4 + wl;
+  if (t >= T) return;                                   // whole wave; no workgroup barrier below
   const bool valid = lane < E;
-  const float z = valid ? logits[t * E + lane] : 0.0f;
-  float m = valid ? z : -INFINITY;
+  const float z = valid ? logits[t * E + lane] : -INFINITY;
+  zs[wl][lane] = z;
+  float m = z;
   for (int o = 1; o < 64; o <<= 1) m = __builtin_fmaxf(m, __shfl_xor(m, o, 64));
   const float p = valid ? expf(z - m) : 0.0f;
   float sum = p;
   for (int o = 1; o < 64; o <<= 1) sum += __shfl_xor(sum, o, 64);
-  bool avail = valid;
-  for (int j = 0; j < k; j++) {
-    float bv = z;
-    int bi = lane;
-    int bo = avail ? 1 : 0;
-    for (int o = 1; o < 64; o <<= 1) {
-      const float v2 = __shfl_xor(bv, o, 64);
-      const int i2 = __shfl_xor(bi, o, 64);
-      const int o2 = __shfl_xor(bo, o, 64);
-      const bool better = o2 && (!bo || v2 > bv || (v2 == bv && i2 < bi));
-      if (better) {
-        bv = v2;
-        bi = i2;
-        bo = o2;
-      }
-    }
-    const float pw = __shfl(p, bi, 64);
-    if (lane == 0) {
-      ids[t * k + j] = bi;
-      wts[t * k + j] = pw / sum;
-    }
-    if (lane == bi) avail = false;
+  // the wave's LDS accesses execute in order: the row is complete here
+  int rank = 0;
+#pragma unroll
+  for (int j = 0; j < 64; j += 4) {
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(&zs[wl][j]);
+#pragma unroll
+    for (int i = 0; i < 4; i++) rank += (v[i] > z || (v[i] == z && j + i < lane)) ? 1 : 0;
+  }
+  if (valid && rank < k) {
+    ids[t * k + rank] = lane;
+    wts[t * k + rank] = p / sum;
   }
 }
 
+// One workgroup per expert e; wave w owns the w-th of 16 contiguous ranges of
+// the T*k (token, slot) pairs, read 64 consecutive pairs per load, a block of
+// GROUP_ROUNDS loads in flight at once.  Pass 1 counts, per wave, the pairs
+// with an expert below e (the workgroup's sum is the expert's first grouped
+// row) and those with expert e; pass 2 places each match at the running
+// position of the wave (ballot and popcount), so the rows of e come out in
+// increasing pair order, which is increasing token order.  When a wave's
+// range is one block (up to 32768 pairs, 4096 tokens x 8) it stays in
+// registers for pass 2.
+constexpr int GROUP_ROUNDS = 32;
+__device__ __forceinline__ void group_load(const int32_t* __restrict__ ids, int64_t base, int64_t p1, int lane,
+                                           int (&v)[GROUP_ROUNDS]) {
+#pragma unroll
+  for (int u = 0; u < GROUP_ROUNDS; u++) {
+    const int64_t i = base + 64 * u + lane;
+    v[u] = i < p1 ? ids[i] : 0x7FFFFFFF;                // past the range: neither below e nor e
+  }
+}
+__device__ __forceinline__ void group_count(const int (&v)[GROUP_ROUNDS], int e, int& lt, int& cnt) {
+#pragma unroll
+  for (int u = 0; u < GROUP_ROUNDS; u++) {
+    lt += v[u] < e ? 1 : 0;
+    cnt += v[u] == e ? 1 : 0;
+  }
+}
+__device__ __forceinline__ void group_place(const int (&v)[GROUP_ROUNDS], int e, int k, int64_t base, int lane,
+                                            int& pos, int32_t* __restrict__ row_token,
+                                            int32_t* __restrict__ row_slot) {
+  const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int u = 0; u < GROUP_ROUNDS; u++) {
+    const bool hit = v[u] == e;
+    const unsigned long long b = __ballot(hit);
+    if (hit) {
+      const int64_t i = base + 64 * u + lane;
+      const int r = pos + __popcll(b & below);
+      row_token[r] = (int32_t)(i / k);
+      row_slot[r] = (int32_t)(i % k);
+    }
+    pos += __popcll(b);
+  }
+}
 __global__ __launch_bounds__(1024) void k_group(const int32_t* __restrict__ ids, int64_t T, int E, int k,
                                                 int32_t* __restrict__ offsets, int32_t* __restrict__ row_token,
                                                 int32_t* __restrict__ row_slot) {
-  __shared__ int red[16];
+  __shared__ int lt_w[16], m_w[16];
   const int e = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t P = T * k;
-  int below = 0;
-  for (int64_t i = tid; i < P; i += 1024) below += ids[i] < e ? 1 : 0;
-  for (int o = 1; o < 64; o <<= 1) below += __shfl_xor(below, o, 64);
-  if (lane == 0) red[wv] = below;
-  __syncthreads();
-  int first = 0;
-  for (int w = 0; w < 16; w++) first += red[w];
-  __syncthreads();
-  int base = first;
-  for (int64_t t0 = 0; t0 < T; t0 += 1024) {
-    const int64_t t = t0 + tid;
-    int slot = -1;
-    if (t < T)
-      for (int j = 0; j < k; j++)
-        if (ids[t * k + j] == e) slot = j;
-    const unsigned long long b = __ballot(slot >= 0);
-    const int pre = __popcll(b & ((1ull << lane) - 1ull));
-    if (lane == 0) red[wv] = __popcll(b);
+  const int64_t per = ((P + 15) / 16 + 63) / 64 * 64;
+  const int64_t p0 = wv * per < P ? wv * per : P;
+  const int64_t p1 = p0 + per < P ? p0 + per : P;
+  constexpr int64_t BLK = 64 * GROUP_ROUNDS;
+  // wave sums of both counts, then the workgroup's: the expert's first row and
+  // the rows of e in the waves before this one
+  auto scan = [&](int lt, int cnt, int& first, int& pos) {
+    for (int o = 1; o < 64; o <<= 1) {
+      lt += __shfl_xor(lt, o, 64);
+      cnt += __shfl_xor(cnt, o, 64);
+    }
+    if (lane == 0) {
+      lt_w[wv] = lt;
+      m_w[wv] = cnt;
+    }
     __syncthreads();
-    int wb = 0, tot = 0;
+    first = 0;
+    pos = 0;
     for (int w = 0; w < 16; w++) {
-      const int c = red[w];
-      wb += w < wv ? c : 0;
-      tot += c;
+      first += lt_w[w];
+      pos += w < wv ? m_w[w] : 0;
     }
-    if (slot >= 0) {
-      row_token[base + wb + pre] = (int32_t)t;
-      row_slot[base + wb + pre] = slot;
+    pos += first;
+    return cnt;
+  };
+  int first, pos, lt = 0, cnt = 0;
+  if (per <= BLK) {                                     // workgroup-uniform: one block per wave
+    int v[GROUP_ROUNDS];
+    group_load(ids, p0, p1, lane, v);
+    group_count(v, e, lt, cnt);
+    if (scan(lt, cnt, first, pos) > 0) group_place(v, e, k, p0, lane, pos, row_token, row_slot);
+  } else {
+    for (int64_t base = p0; base < p1; base += BLK) {
+      int v[GROUP_ROUNDS];
+      group_load(ids, base, p1, lane, v);
+      group_count(v, e, lt, cnt);
     }
-    base += tot;
-    __syncthreads();
+    if (scan(lt, cnt, first, pos) > 0)
+      for (int64_t base = p0; base < p1; base += BLK) {
+        int v[GROUP_ROUNDS];
+        group_load(ids, base, p1, lane, v);
+        group_place(v, e, k, base, lane, pos, row_token, row_slot);
+      }
   }
   if (tid == 0) {
     offsets[e] = first;
