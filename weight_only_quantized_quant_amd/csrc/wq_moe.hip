@@ -182,12 +182,37 @@ __global__ __launch_bounds__(1024) void k_group(const int32_t* __restrict__ ids,
 // ---------------------------------------------------------------------------
 // Scale recipe, weight re-layout, tables
 // ---------------------------------------------------------------------------
-// One wave per output channel: ch = 8 * RN(amax / 448) (1 for an all-zero
-// channel), s8 = e4m3(RN(s / ch)) with correctly rounded division.
+// Per output channel: ch = 8 * RN(amax / 448) (1 for an all-zero channel),
+// s8 = e4m3(RN(s / ch)) with correctly rounded division.  Channels of at most
+// 32 groups share a wave, gp lanes each (gp the smallest power of two >= G,
+// the maximum an xor butterfly within the gp lanes); longer channels take one
+// wave each.
+inline int scales_lanes(int G) {
+  int gp = 1;
+  while (gp < G) gp <<= 1;
+  return gp;
+}
 __global__ __launch_bounds__(256) void k_w4a8_scales(const uint16_t* __restrict__ sc, int64_t rows, int G,
                                                      uint8_t* __restrict__ s8, float* __restrict__ ch) {
   const int lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (G <= 32) {
+    int gp = 1;
+    while (gp < G) gp <<= 1;
+    const int64_t r = wave * (64 / gp) + lane / gp;
+    const int g = lane % gp;
+    const bool live = r < rows && g < G;
+    const float v = live ? bf16_to_f32(sc[r * G + g]) : 0.0f;
+    float amax = __builtin_fabsf(v);
+    for (int o = 1; o < gp; o <<= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, o, 64));
+    float s = amax / 448.0f;
+    if (s == 0.0f) s = 1.0f;
+    const float c = 8.0f * s;
+    if (live) s8[r * G + g] = (uint8_t)(e4m3_pack2<false>(clamp448(v / c), 0.0f, 0u) & 0xFFu);
+    if (live && g == 0) ch[r] = c;
+    return;
+  }
+  const int64_t r = wave;
   if (r >= rows) return;
   float amax = 0.0f;
   for (int g = lane; g < G; g += 64) amax = __builtin_fmaxf(amax, __builtin_fabsf(bf16_to_f32(sc[r * G + g])));
@@ -553,7 +578,8 @@ wq_status wq_w4a8_prepack(const uint32_t* wq, const uint16_t* scales, int64_t ex
   if (!wq_numel_ok(experts * N, K)) return WQ_EINVAL;
   hipStream_t s = (hipStream_t)stream;
   const int64_t rows = experts * N, G = K / 128, words = rows * (K / 8);
-  k_w4a8_scales<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(scales, rows, (int)G, s8, ch);
+  const int64_t scale_waves = G <= 32 ? (rows + 64 / scales_lanes((int)G) - 1) / (64 / scales_lanes((int)G)) : rows;
+  k_w4a8_scales<<<(unsigned)((scale_waves + 3) / 4), 256, 0, s>>>(scales, rows, (int)G, s8, ch);
   k_w4a8_relayout<<<(unsigned)((words / 4 + 255) / 256), 256, 0, s>>>(wq, wq_out, words);
   return wq_launch_status();
 }
