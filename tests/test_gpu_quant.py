@@ -84,7 +84,10 @@ def test_e4m3_block(W, block, bf16):
     assert np.array_equal(host_u8(codes), wc)
 
 
-@pytest.mark.parametrize("shape", [(5, 4096), (3, 136), (64, 1536), (1, 8)])
+# rows held in registers in 1, 2 or 4 rounds of 2048 elements (up to 8192
+# columns, each bound crossed) and longer rows read twice
+@pytest.mark.parametrize("shape", [(5, 4096), (3, 136), (64, 1536), (1, 8), (2, 2056), (9, 6144), (4, 8192),
+                                   (7, 8200), (3, 20000)])
 def test_e4m3_per_row(W, shape):
     a = _wide(shape, seed=shape[1], block=8)
     bits = to_bf16_bits(a)

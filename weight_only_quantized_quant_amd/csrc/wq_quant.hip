@@ -121,6 +121,52 @@ __global__ __launch_bounds__(kThreads) void k_e4m3_row(const void* __restrict__ 
   if (threadIdx.x == 0) scales[row] = s;
 }
 
+// The same for rows of at most R * 2048 elements: every thread loads its R
+// pieces of 8 at once and keeps them in registers for the quantization, so
+// the row is read once and the loads are all in flight together.
+template <bool BF16, int R>
+__global__ __launch_bounds__(kThreads) void k_e4m3_row_reg(const void* __restrict__ x, int64_t cols,
+                                                          uint8_t* __restrict__ codes, float* __restrict__ scales) {
+  __shared__ float red[kThreads / 64];
+  const int64_t row = blockIdx.x;
+  const int64_t base = row * cols;
+  float v[R][8];
+#pragma unroll
+  for (int r = 0; r < R; r++) {
+    const int64_t c = (int64_t)(r * kThreads + threadIdx.x) * 8;
+    if (c < cols) {
+      load8<BF16>(x, base + c, v[r]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; i++) v[r][i] = 0.0f;
+    }
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int r = 0; r < R; r++) m = __builtin_fmaxf(m, absmax8(v[r]));
+  m = group_max(m, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+  float s = m / 448.0f;
+  if (s == 0.0f) s = 1.0f;
+  const float y = 1.0f / s;
+  const bool fast = s >= 0x1p-90f && s <= 0x1p90f;
+#pragma unroll
+  for (int r = 0; r < R; r++) {
+    const int64_t c = (int64_t)(r * kThreads + threadIdx.x) * 8;
+    if (c < cols) {
+      float q[8];
+#pragma unroll
+      for (int i = 0; i < 8; i++) q[i] = fast ? div_rn_markstein(v[r][i], s, y) : clamp448(v[r][i] / s);
+      uint32_t r0 = e4m3_pack2<true>(q[2], q[3], e4m3_pack2<false>(q[0], q[1], 0u));
+      uint32_t r1 = e4m3_pack2<true>(q[6], q[7], e4m3_pack2<false>(q[4], q[5], 0u));
+      *reinterpret_cast<u32x2_t*>(codes + base + c) = u32x2_t{r0, r1};
+    }
+  }
+  if (threadIdx.x == 0) scales[row] = s;
+}
+
 // ---------------------------------------------------------------------------
 // MXFP4: 16 elements per thread; block 32 -> lane pairs, block 16 -> one lane.
 // ---------------------------------------------------------------------------
@@ -441,8 +487,21 @@ wq_status quantize_e4m3(const void* x, int x_dtype, int64_t rows, int64_t cols, 
   if (!scales) return WQ_EINVAL;
   if (block == -1) {
     if (rows > 0x7FFFFFFF) return WQ_EINVAL;
-    if (bf) k_e4m3_row<true><<<(unsigned)rows, kThreads, 0, s>>>(x, cols, codes, scales);
-    else k_e4m3_row<false><<<(unsigned)rows, kThreads, 0, s>>>(x, cols, codes, scales);
+    const unsigned g = (unsigned)rows;
+    constexpr int64_t PIECE = kThreads * 8;            // elements per register round of a row
+    if (cols <= PIECE) {
+      if (bf) k_e4m3_row_reg<true, 1><<<g, kThreads, 0, s>>>(x, cols, codes, scales);
+      else k_e4m3_row_reg<false, 1><<<g, kThreads, 0, s>>>(x, cols, codes, scales);
+    } else if (cols <= 2 * PIECE) {
+      if (bf) k_e4m3_row_reg<true, 2><<<g, kThreads, 0, s>>>(x, cols, codes, scales);
+      else k_e4m3_row_reg<false, 2><<<g, kThreads, 0, s>>>(x, cols, codes, scales);
+    } else if (cols <= 4 * PIECE) {
+      if (bf) k_e4m3_row_reg<true, 4><<<g, kThreads, 0, s>>>(x, cols, codes, scales);
+      else k_e4m3_row_reg<false, 4><<<g, kThreads, 0, s>>>(x, cols, codes, scales);
+    } else {
+      if (bf) k_e4m3_row<true><<<g, kThreads, 0, s>>>(x, cols, codes, scales);
+      else k_e4m3_row<false><<<g, kThreads, 0, s>>>(x, cols, codes, scales);
+    }
     return wq_launch_status();
   }
   if (block != 16 && block != 32 && block != 64 && block != 128 && block != 256) return WQ_EUNSUPPORTED;
