@@ -153,3 +153,29 @@ def test_moe_graph_replays(W):
 
     _replay_matches(0x44, run, run, [y], [ref], lambda: W.wq_moe_route(logits, k))
     assert torch.equal(held["ids"], ids_r) and torch.equal(held["off"], off_r)
+
+
+def test_launches_follow_the_callers_stream(W):
+    """Every entry point enqueues on the stream current at the call: a decode
+    GEMV and a quantizer issued on a side stream (default priority), behind a
+    busy kernel on that stream, are complete and equal to the default-stream
+    results once that stream alone has been synchronised."""
+    banner("side-stream launches: wq_gemm int4 M=2 and quantize_mxfp4")
+    xbits, Wf = decode_inputs(2, K=2048, N=3000, seed=13)
+    x = dev_bf16(xbits)
+    wq, wdt, sc, sdt, group = _weights(W, "int4", Wf)
+    a = x.float().repeat(8, 1).to(torch.bfloat16).contiguous()
+    ref_y = W.wq_gemm(x, wq, wdt, sc, sdt, group, 3000)
+    ref_c, ref_s = W.quantize_mxfp4(a, 32)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    y = torch.full_like(ref_y, 7.0)
+    c, s = torch.zeros_like(ref_c), torch.zeros_like(ref_s)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        W.wq_util_spin(200000)
+        W.wq_gemm(x, wq, wdt, sc, sdt, group, 3000, y=y)
+        W.quantize_mxfp4(a, 32, codes=c, scales=s)
+    side.synchronize()
+    assert torch.equal(_bits(y), _bits(ref_y))
+    assert torch.equal(c, ref_c) and torch.equal(s, ref_s)
