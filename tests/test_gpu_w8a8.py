@@ -172,8 +172,24 @@ def test_gemm_full_size_sampled_rows(W):
     bc, sb = O8.quantize_e4m3_block2d(Wf)
     banner("w8a8 full size 8192x4096 . 14336x4096, group x block")
     y = W.wq_gemm_w8a8(dev_u8(ac), dev_f32(sa.reshape(-1)), 32, 1, dev_u8(bc), dev_f32(sb.reshape(-1)), 32, 1, 128)
-    rows = np.unique(np.concatenate([[0, 255, 256, 8191], np.random.default_rng(96).choice(8192, 60, replace=False)]))
+    # both rows at every 256-row tile boundary and 512 seed-chosen rows
+    edges = np.concatenate([np.arange(0, 8192, 256), np.arange(255, 8192, 256)])
+    rows = np.unique(np.concatenate([edges, np.random.default_rng(96).choice(8192, 512, replace=False)]))
     _check(y, ac, O8.expand_scales(sa, 8192, 32), bc, O8.expand_scales(sb, 14336, 32, 128), rows=rows)
+
+
+def test_gemm_full_size_token_channel_sampled_rows(W):
+    # M = 8192, K = 4096, N = 14336: per-token activations x per-channel weights
+    # (the scales factor out of the K sum and apply in the epilogue)
+    xbits, Wf = prefill_inputs(0)
+    x = bf16_bits_to_f32(xbits)
+    ac, sa = OE.quantize_e4m3(x, -1)
+    bc, sb = OE.quantize_e4m3(Wf, -1)
+    banner("w8a8 full size 8192x4096 . 14336x4096, token x channel")
+    y = W.wq_gemm_w8a8(dev_u8(ac), dev_f32(sa[:, 0]), 1, 0, dev_u8(bc), dev_f32(sb[:, 0]), 1, 0, 1)
+    edges = np.concatenate([np.arange(0, 8192, 256), np.arange(255, 8192, 256)])
+    rows = np.unique(np.concatenate([edges, np.random.default_rng(97).choice(8192, 512, replace=False)]))
+    _check(y, ac, O8.expand_scales(sa[:, 0], 8192, 32), bc, O8.expand_scales(sb[:, 0], 14336, 32), rows=rows)
 
 
 def test_gemm_rejects_short_scale_arrays(W):
