@@ -96,9 +96,11 @@ def test_gemv_tile_rounds(W, kind, M, N, K):
     ("int4", 64, 2, 17, 4096),        # one full tile of 16 rows and one of 1
     ("mxfp4", 32, 2, 4105, 8192),
     ("mxfp4", 32, 1, 14336, 4096),
+    ("int4", 128, 1, 33000, 2048),    # 2063 tiles, 8 rounds over 256 CUs: the last 15 tiles become 30 halves
+    ("int4", 128, 3, 40000, 1024),    # 2500 tiles, a last round of 196 kept as full tiles
 ])
 def test_gemv_more_shapes(W, kind, group, M, N, K):
-    # N from 17 to 16400 with ragged last tiles and balancing rounds of 8-row
+    # N from 17 to 40000 with ragged last tiles and balancing rounds of 8-row
     # tiles, K from 2048 to 14336, scale groups 32 to 128, M = 1-4
     g = np.random.default_rng(M * 11 + N + K + group)
     Wf = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
